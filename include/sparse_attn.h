@@ -1,0 +1,147 @@
+/*
+ * sparse_attn.h -- C ABI of the causal structured-sparse attention library
+ * for AMD Instinct MI355X (gfx950).  Library: libsparse_attn.so.
+ *
+ * Operation.  For every query position i the library takes ONE softmax over
+ * an explicit key set and returns the weighted sum of the value rows:
+ *
+ *   o_i = sum_{j in K(i)} softmax_j( <q_i, k_j> / sqrt(d) + prior(i, j) ) v_j
+ *
+ * with the key set K(i) fixed by the mode:
+ *
+ *   SA_MODE_PI      pi-Attention ("pi-Attention: Periodic Sparse Transformers
+ *                   for Efficient Long-Context Modeling", section 2, items
+ *                   1-3): the causal window [max(0, i-k_win), i] united with
+ *                   the periodic skip keys i - m*pi, m = 1..M, i - m*pi >= 0.
+ *                   A skip position inside the window counts once, as a local
+ *                   key.  Gate alpha (per query token and query head) enters
+ *                   as a log-prior: log(alpha) on local scores, log(1-alpha)
+ *                   on skip scores.  alpha must lie in (0, 1]; alpha = 1
+ *                   removes the skip keys.
+ *   SA_MODE_WINDOW  window-only sparse attention ("LT2: Linear-Time Looped
+ *                   Transformers", section 2.1): the causal window alone, no
+ *                   prior (the same as SA_MODE_PI with M = 0).
+ *   SA_MODE_ECP     paired-half-segment attention ("Efficient Context
+ *                   Propagating Perceiver Architectures for Auto-Regressive
+ *                   Language Modeling", section 2, PAR block): a query in
+ *                   half-segment c = floor(i / seg) attends the keys of
+ *                   half-segments c-1 and c, causally: [max(0,(c-1)*seg), i].
+ *
+ * Grouped-query attention (the attention branch of the hybrid GSS-Transformer
+ * page, methodology item 1): query head h reads key/value head
+ * h / (Hq / Hkv).
+ *
+ * Conventions shared by every entry point.
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous.
+ *     q/k/v/o/caches must be 16-byte aligned, alpha/lens 4-byte aligned.
+ *   - dtype SA_DTYPE_BF16: q, k, v, o (and caches) hold bfloat16; scores,
+ *     softmax and accumulation run in fp32; o is rounded to nearest even.
+ *     dtype SA_DTYPE_F32: everything is fp32.  alpha is fp32 in both.
+ *   - Head dimension d must be 64 or 128 (else SA_ERR_UNSUPPORTED).
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     allocates no device memory and never synchronises.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL =
+ *     the default stream).  The return value only reports argument and launch
+ *     errors; a fault inside a kernel surfaces at the caller's next
+ *     synchronisation.
+ *   - Argument errors are detected on the host before any HIP call, and then
+ *     nothing is launched.  sparse_attn_last_error() gives the detail (per
+ *     thread).  NaN/Inf in the data propagate without checks; alpha outside
+ *     (0, 1] gives undefined (non-finite) outputs for the affected rows.
+ *   - Parameters a mode does not use are ignored (PI: k_win, pi, M, alpha;
+ *     WINDOW: k_win; ECP: seg).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SA_OK 0
+#define SA_ERR_INVALID (-1)     /* bad pointer, size, parameter, alignment or aliasing */
+#define SA_ERR_UNSUPPORTED (-2) /* head dim or dtype outside what is built */
+#define SA_ERR_HIP (-3)         /* a HIP launch or query failed */
+#define SA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
+
+/* Modes. */
+#define SA_MODE_PI 0
+#define SA_MODE_WINDOW 1
+#define SA_MODE_ECP 2
+
+/* I/O element types. */
+#define SA_DTYPE_F32 0
+#define SA_DTYPE_BF16 1
+
+/*
+ * Bytes of device workspace sparse_attn_fwd needs for these arguments (0 when
+ * none is needed: WINDOW, ECP, and PI when no query has a skip key).  Returns
+ * 0 as well for arguments sparse_attn_fwd would reject.
+ */
+size_t sparse_attn_fwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype,
+                                      int mode, int k_win, int pi, int M, int seg);
+
+/*
+ * Prefill forward.
+ *   q     [B, Hq,  N, d]   k, v [B, Hkv, N, d]   o [B, Hq, N, d] (dtype)
+ *   alpha [B, Hq, N] fp32, required when mode == SA_MODE_PI and M > 0 (may be
+ *         NULL otherwise).
+ *   Requires B, Hq, Hkv, N >= 1, Hq % Hkv == 0, k_win >= 0; for PI with M > 0
+ *   pi >= 1; M >= 0; for ECP seg >= 1.  o must not overlap q, k, v, alpha or
+ *   the workspace.
+ *   workspace: device buffer of at least sparse_attn_fwd_workspace_size(...)
+ *   bytes, 256-byte aligned (NULL allowed when that size is 0).  Its contents
+ *   are scratch; it must not be shared by calls that may run concurrently.
+ * Returns SA_OK or an error code.
+ */
+int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *alpha, void *o,
+                    int B, int Hq, int Hkv, int N, int d, int dtype,
+                    int mode, int k_win, int pi, int M, int seg,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace sparse_attn_decode needs (never 0 for valid
+ * arguments; 0 for arguments sparse_attn_decode would reject).
+ */
+size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d, int dtype,
+                                         int mode, int k_win, int pi, int M, int seg);
+
+/*
+ * Single-token decode over a KV cache (autoregressive decoding, where the
+ * pi-Attention page restricts every key to earlier positions).  For sequence
+ * b the new token's query sits at position i = cache_lens[b] - 1 and the
+ * cache already holds that token's key and value; the query attends K(i) of
+ * the mode, read from rows [b, h / (Hq/Hkv), j, :] of the caches.
+ *   q          [B, Hq, d]               o [B, Hq, d] (dtype)
+ *   k_cache, v_cache [B, Hkv, Lmax, d]  (the prefill k/v layout with N = Lmax)
+ *   cache_lens [B] int32, DEVICE memory; each value must lie in [1, Lmax].
+ *              A row whose length lies outside that range reads nothing and
+ *              gets NaN outputs.
+ *   alpha      [B, Hq] fp32 (PI with M > 0; NULL allowed otherwise).
+ *   workspace  >= sparse_attn_decode_workspace_size(...) bytes, 256-byte
+ *              aligned; scratch, not to be shared by concurrent calls.
+ * Returns SA_OK or an error code.
+ */
+int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                       const int *cache_lens, const float *alpha, void *o,
+                       int B, int Hq, int Hkv, int Lmax, int d, int dtype,
+                       int mode, int k_win, int pi, int M, int seg,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *sparse_attn_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *sparse_attn_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int sparse_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

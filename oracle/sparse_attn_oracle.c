@@ -1,0 +1,290 @@
+/*
+ * sparse_attn_oracle.c -- plain fp64 CPU oracle for causal structured-sparse
+ * attention (forward and single-token decode).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or constant with
+ * the HIP library; it is written from the method's definition, not from the
+ * GPU kernels.
+ *
+ * What it computes.  For one query position i the method forms an explicit
+ * key set and takes ONE softmax over it:
+ *
+ *   - pi-Attention ("pi-Attention: Periodic Sparse Transformers for
+ *     Efficient Long-Context Modeling", section 2, items 1-3): a causal
+ *     local window j in [i-k, i] plus the periodic skip keys j = i - m*pi,
+ *     m = 1..M, j >= 0.  The page gives the window as i-k..i+k; causal
+ *     decoding restricts it to earlier positions, so the causal reading
+ *     [i-k, i] is used.  The union is a set: a skip key that already lies in
+ *     the window is the window's key (it gets the local prior once).  A
+ *     per-token, per-head gate alpha in (0, 1] enters as a log-prior:
+ *     log(alpha) is added to the scores of local keys and log(1 - alpha) to
+ *     the scores of skip keys before the single softmax.
+ *   - Window-only attention ("LT2: Linear-Time Looped Transformers",
+ *     section 2.1, sparse variant): the window alone, no prior.
+ *   - ECP paired-half-segment attention ("Efficient Context Propagating
+ *     Perceiver Architectures for Auto-Regressive Language Modeling",
+ *     section 2, PAR block): a query in half-segment c = floor(i/s) sees the
+ *     keys of half-segments c-1 and c, causally masked, i.e.
+ *     j in [max(0, (c-1)*s), i].  No prior.
+ *
+ *   score(i, j) = <q_i, k_j> / sqrt(d) + prior(i, j)
+ *   o_i        = sum_j exp(score(i,j) - max) v_j / sum_j exp(score(i,j) - max)
+ *
+ * Everything is evaluated in double precision with libm exp/log.  Inputs are
+ * fp32 arrays (bf16 inputs are widened exactly by the caller).  Grouped-query
+ * attention ("Long-context modelling with a hybrid GSS-Transformer",
+ * methodology item 1): query head h reads key/value head h / (Hq / Hkv).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_MODE_PI 0
+#define ORC_MODE_WINDOW 1
+#define ORC_MODE_ECP 2
+
+#define ORC_LOCAL 0
+#define ORC_SKIP 1
+
+#define ORC_OK 0
+#define ORC_ERR_ARGS -1
+#define ORC_ERR_ALPHA -2
+#define ORC_ERR_NOMEM -3
+
+static int64_t orc_max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+/* Number of keys the key set of any query can hold (upper bound). */
+int64_t orc_key_capacity(int mode, int64_t k_win, int64_t M, int64_t seg)
+{
+    if (mode == ORC_MODE_ECP) return 2 * seg;
+    if (mode == ORC_MODE_WINDOW) return k_win + 1;
+    return k_win + 1 + (M > 0 ? M : 0);
+}
+
+/*
+ * Key set of query position i, in ascending order of position, with the
+ * label ORC_LOCAL or ORC_SKIP for each key.  Returns the number of keys, or
+ * -1 when cap is too small or the parameters are invalid.
+ *   PI / WINDOW: pi-Attention section 2 items 1-2; LT2 section 2.1.
+ *   ECP: ECP section 2 (queries of the current half-segment, keys and values
+ *   of the current and the previous half-segment), causal.
+ */
+int64_t orc_key_set(int64_t i, int mode, int64_t k_win, int64_t pi, int64_t M,
+                    int64_t seg, int64_t *keys, int32_t *labels, int64_t cap)
+{
+    int64_t n = 0, lo, j, m;
+    if (i < 0) return -1;
+    if (mode == ORC_MODE_ECP) {
+        if (seg <= 0) return -1;
+        lo = orc_max64(0, (i / seg - 1) * seg);
+    } else if (mode == ORC_MODE_PI || mode == ORC_MODE_WINDOW) {
+        if (k_win < 0) return -1;
+        lo = orc_max64(0, i - k_win);
+    } else {
+        return -1;
+    }
+    /* Skip keys lie below the window: i - m*pi for m = M down to 1, keeping
+       those at or above position 0 and strictly below the window start (a
+       key inside the window belongs to the window). */
+    if (mode == ORC_MODE_PI && M > 0) {
+        if (pi <= 0) return -1;
+        for (m = M; m >= 1; --m) {
+            j = i - m * pi;
+            if (j < 0 || j >= lo) continue;
+            if (n >= cap) return -1;
+            keys[n] = j;
+            labels[n] = ORC_SKIP;
+            ++n;
+        }
+    }
+    for (j = lo; j <= i; ++j) {
+        if (n >= cap) return -1;
+        keys[n] = j;
+        labels[n] = ORC_LOCAL;
+        ++n;
+    }
+    return n;
+}
+
+/*
+ * One query row: softmax over the explicit key set with the log-prior, then
+ * the weighted sum of value rows.  qrow has d entries; kmat/vmat point at row
+ * 0 of the key/value head (row stride d).  log_local/log_skip are the priors
+ * (0 for modes without a gate).  Writes d doubles to out.
+ */
+static void orc_row(const float *qrow, const float *kmat, const float *vmat,
+                    int64_t d, double log_local, double log_skip,
+                    const int64_t *keys, const int32_t *labels, int64_t n,
+                    double *score, double *out)
+{
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double mx = -INFINITY, denom = 0.0;
+    int64_t t, c;
+    for (t = 0; t < n; ++t) {
+        const float *krow = kmat + keys[t] * d;
+        double dot = 0.0;
+        for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)krow[c];
+        score[t] = dot * inv_sqrt_d + (labels[t] == ORC_LOCAL ? log_local : log_skip);
+        if (score[t] > mx) mx = score[t];
+    }
+    for (c = 0; c < d; ++c) out[c] = 0.0;
+    for (t = 0; t < n; ++t) {
+        const float *vrow = vmat + keys[t] * d;
+        double w = exp(score[t] - mx);
+        denom += w;
+        for (c = 0; c < d; ++c) out[c] += w * (double)vrow[c];
+    }
+    for (c = 0; c < d; ++c) out[c] /= denom;
+}
+
+static int orc_check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int mode,
+                            int64_t k_win, int64_t pi, int64_t M, int64_t seg)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return ORC_ERR_ARGS;
+    if (mode == ORC_MODE_ECP) return seg > 0 ? ORC_OK : ORC_ERR_ARGS;
+    if (mode != ORC_MODE_PI && mode != ORC_MODE_WINDOW) return ORC_ERR_ARGS;
+    if (k_win < 0) return ORC_ERR_ARGS;
+    if (mode == ORC_MODE_PI && (M < 0 || (M > 0 && pi <= 0))) return ORC_ERR_ARGS;
+    return ORC_OK;
+}
+
+/* Priors of one row.  alpha must lie in (0, 1]; alpha = 1 makes the skip
+   prior log(0) = -inf, which removes the skip keys from the softmax. */
+static int orc_priors(int mode, const float *alpha, int64_t at, double *lp, double *ls)
+{
+    double a;
+    *lp = 0.0;
+    *ls = 0.0;
+    if (mode != ORC_MODE_PI) return ORC_OK;
+    if (alpha == NULL) return ORC_ERR_ALPHA;
+    a = (double)alpha[at];
+    if (!(a > 0.0 && a <= 1.0)) return ORC_ERR_ALPHA;
+    *lp = log(a);
+    *ls = log(1.0 - a); /* -inf at a == 1 */
+    return ORC_OK;
+}
+
+/*
+ * Forward attention for a selection of query rows.
+ *   q     [B, Hq, N, d]  fp32      k, v [B, Hkv, N, d] fp32
+ *   alpha [B, Hq, N]     fp32 (PI only; may be NULL otherwise)
+ *   sel   nsel flat row ids (b*Hq + h)*N + i, or NULL for every row in order
+ *   out   [nsel, d] doubles (or [B, Hq, N, d] when sel is NULL)
+ * Returns ORC_OK or a negative error code.
+ */
+int orc_fwd_rows(const float *q, const float *k, const float *v, const float *alpha,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                 const int64_t *sel, int64_t nsel, double *out)
+{
+    int64_t cap, total, r;
+    int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
+    if (err != ORC_OK || N <= 0) return ORC_ERR_ARGS;
+    total = B * Hq * N;
+    if (sel == NULL) nsel = total;
+    cap = orc_key_capacity(mode, k_win, M, seg);
+    err = ORC_OK;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc((size_t)cap * sizeof(int64_t));
+        int32_t *labels = (int32_t *)malloc((size_t)cap * sizeof(int32_t));
+        double *score = (double *)malloc((size_t)cap * sizeof(double));
+        int local_err = (keys && labels && score) ? ORC_OK : ORC_ERR_NOMEM;
+#pragma omp for schedule(dynamic, 64)
+        for (r = 0; r < nsel; ++r) {
+            int64_t row = sel ? sel[r] : r, b, h, i, g, n;
+            double lp, ls;
+            if (local_err != ORC_OK) continue;
+            if (row < 0 || row >= total) { local_err = ORC_ERR_ARGS; continue; }
+            i = row % N;
+            h = (row / N) % Hq;
+            b = row / (N * Hq);
+            g = h / (Hq / Hkv);
+            if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) continue;
+            n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+            if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
+            orc_row(q + row * d, k + (b * Hkv + g) * N * d, v + (b * Hkv + g) * N * d,
+                    d, lp, ls, keys, labels, n, score, out + r * d);
+        }
+        if (local_err != ORC_OK) {
+#pragma omp critical
+            err = local_err;
+        }
+        free(keys);
+        free(labels);
+        free(score);
+    }
+    return err;
+}
+
+/*
+ * Single-token decode over a KV cache: for every sequence b and query head h
+ * the query sits at position i = lens[b] - 1 and attends the key set of i,
+ * read from the cache rows [b, g, j, :] (the cache already holds the new
+ * token's key and value).
+ *   q     [B, Hq, d]          kc, vc [B, Hkv, Lmax, d]     lens [B] int32
+ *   alpha [B, Hq] (PI only)   out    [B, Hq, d] doubles
+ */
+int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *lens,
+               const float *alpha, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax,
+               int64_t d, int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+               double *out)
+{
+    int64_t cap, r;
+    int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
+    if (err != ORC_OK || Lmax <= 0) return ORC_ERR_ARGS;
+    for (r = 0; r < B; ++r)
+        if (lens[r] < 1 || lens[r] > Lmax) return ORC_ERR_ARGS;
+    cap = orc_key_capacity(mode, k_win, M, seg);
+    err = ORC_OK;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc((size_t)cap * sizeof(int64_t));
+        int32_t *labels = (int32_t *)malloc((size_t)cap * sizeof(int32_t));
+        double *score = (double *)malloc((size_t)cap * sizeof(double));
+        int local_err = (keys && labels && score) ? ORC_OK : ORC_ERR_NOMEM;
+#pragma omp for schedule(dynamic, 1)
+        for (r = 0; r < B * Hq; ++r) {
+            int64_t b = r / Hq, h = r % Hq, g = h / (Hq / Hkv), i = lens[b] - 1, n;
+            double lp, ls;
+            if (local_err != ORC_OK) continue;
+            if ((local_err = orc_priors(mode, alpha, r, &lp, &ls)) != ORC_OK) continue;
+            n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+            if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
+            orc_row(q + r * d, kc + (b * Hkv + g) * Lmax * d, vc + (b * Hkv + g) * Lmax * d,
+                    d, lp, ls, keys, labels, n, score, out + r * d);
+        }
+        if (local_err != ORC_OK) {
+#pragma omp critical
+            err = local_err;
+        }
+        free(keys);
+        free(labels);
+        free(score);
+    }
+    return err;
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -1,0 +1,212 @@
+"""ctypes binding over libsparse_attn.so (C ABI in include/sparse_attn.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  torch supplies device memory (outputs, workspace) and the
+current stream.  There is no fallback: if the library is missing or a tensor
+is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+MODE_PI = 0
+MODE_WINDOW = 1
+MODE_ECP = 2
+_MODES = {"pi": MODE_PI, "window": MODE_WINDOW, "ecp": MODE_ECP}
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+_DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+_lock = threading.Lock()
+_lib = None
+
+EXPORTED = ("sparse_attn_fwd_workspace_size", "sparse_attn_fwd",
+            "sparse_attn_decode_workspace_size", "sparse_attn_decode",
+            "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_version")
+
+
+class SparseAttnError(RuntimeError):
+    """A launch or HIP failure reported by the library."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsparse_attn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libsparse_attn.so is not built (%s); run "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        lib.sparse_attn_fwd_workspace_size.restype = sz
+        lib.sparse_attn_fwd_workspace_size.argtypes = [i] * 11
+        lib.sparse_attn_fwd.restype = i
+        lib.sparse_attn_fwd.argtypes = [vp] * 5 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_decode_workspace_size.restype = sz
+        lib.sparse_attn_decode_workspace_size.argtypes = [i] * 11
+        lib.sparse_attn_decode.restype = i
+        lib.sparse_attn_decode.argtypes = [vp] * 6 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_status_string.restype = ctypes.c_char_p
+        lib.sparse_attn_status_string.argtypes = [i]
+        lib.sparse_attn_last_error.restype = ctypes.c_char_p
+        lib.sparse_attn_last_error.argtypes = []
+        lib.sparse_attn_version.restype = i
+        lib.sparse_attn_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _raise(lib, rc: int, what: str):
+    detail = lib.sparse_attn_last_error().decode()
+    msg = "%s: %s (%s)" % (what, lib.sparse_attn_status_string(rc).decode(), detail)
+    if rc in (SA_ERR_INVALID, SA_ERR_WORKSPACE):
+        raise ValueError(msg)
+    if rc == SA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise SparseAttnError(msg)
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        return _MODES[mode.lower()]
+    return int(mode)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (got %s)" % t.device)
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd_workspace_size(B, Hq, Hkv, N, d, dtype, mode, k_win=0, pi=0, M=0, seg=0) -> int:
+    lib = load_library()
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.sparse_attn_fwd_workspace_size(B, Hq, Hkv, N, d, dt, _mode(mode),
+                                                  k_win, pi, M, seg))
+
+
+def decode_workspace_size(B, Hq, Hkv, Lmax, d, dtype, mode, k_win=0, pi=0, M=0, seg=0) -> int:
+    lib = load_library()
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.sparse_attn_decode_workspace_size(B, Hq, Hkv, Lmax, d, dt, _mode(mode),
+                                                     k_win, pi, M, seg))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return workspace
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
+        out=None, workspace=None):
+    """Prefill forward: q [B,Hq,N,d], k/v [B,Hkv,N,d] (bf16 or fp32, on the
+    GPU), alpha [B,Hq,N] fp32 for the gated mode.  Returns o [B,Hq,N,d]."""
+    lib = load_library()
+    _need_gpu(q, k, v, alpha, out, workspace)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d [B, H, N, d]")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise NotImplementedError("q, k, v must share dtype bf16 or fp32")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k/v shape %s/%s does not match q %s" % (tuple(k.shape), tuple(v.shape),
+                                                                 tuple(q.shape)))
+    m = _mode(mode)
+    if alpha is not None:
+        if alpha.dtype != torch.float32 or tuple(alpha.shape) != (B, Hq, N):
+            raise ValueError("alpha must be fp32 [B, Hq, N]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    dt = _DTYPES[q.dtype]
+    nbytes = int(lib.sparse_attn_fwd_workspace_size(B, Hq, Hkv, N, d, dt, m, k_win, pi, M, seg))
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(out),
+                             B, Hq, Hkv, N, d, dt, m, int(k_win), int(pi), int(M), int(seg),
+                             _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
+    if rc != SA_OK:
+        _raise(lib, rc, "sparse_attn_fwd")
+    return out
+
+
+def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
+           M: int = 0, seg: int = 0, out=None, workspace=None):
+    """Single-token decode: q [B,Hq,d], caches [B,Hkv,Lmax,d], cache_lens [B]
+    int32 on the GPU, alpha [B,Hq] fp32 for the gated mode.  Returns o [B,Hq,d]."""
+    lib = load_library()
+    _need_gpu(q, k_cache, v_cache, cache_lens, alpha, out, workspace)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and caches [B, Hkv, Lmax, d]")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise NotImplementedError("q and caches must share dtype bf16 or fp32")
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Lmax, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    if alpha is not None and (alpha.dtype != torch.float32 or tuple(alpha.shape) != (B, Hq)):
+        raise ValueError("alpha must be fp32 [B, Hq]")
+    m = _mode(mode)
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _DTYPES[q.dtype]
+    nbytes = int(lib.sparse_attn_decode_workspace_size(B, Hq, Hkv, Lmax, d, dt, m, k_win, pi,
+                                                       M, seg))
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.sparse_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
+                                _ptr(alpha), _ptr(out), B, Hq, Hkv, Lmax, d, dt, m,
+                                int(k_win), int(pi), int(M), int(seg), _ptr(ws),
+                                nbytes if ws is not None else 0, _stream(q.device))
+    if rc != SA_OK:
+        _raise(lib, rc, "sparse_attn_decode")
+    return out
+
+
+def loop_fwd(q, k, v, alpha=None, *, steps: int, mode, k_win: int = 0, pi: int = 0, M: int = 0,
+             seg: int = 0, outs=None, workspace=None):
+    """Looped block: apply the attention ``steps`` times with q, k fixed, the
+    output of one application becoming the value input of the next ("LT2",
+    section 1 and section 2.2).  Two ping-pong output buffers are used (an
+    output never aliases its own value input).  Returns the last output."""
+    if outs is None:
+        outs = (torch.empty_like(q), torch.empty_like(q) if steps > 1 else None)
+    vin = v
+    o = None
+    for t in range(steps):
+        o = fwd(q, k, vin, alpha, mode=mode, k_win=k_win, pi=pi, M=M, seg=seg,
+                out=outs[t % 2], workspace=workspace)
+        vin = o
+    return o
