@@ -1,0 +1,237 @@
+// api.hip -- the C ABI of libsparse_attn (declared in include/sparse_attn.h):
+// argument validation on the host (before any HIP call), workspace sizing,
+// and the launch sequence on the caller's stream.  No allocation, no
+// synchronisation, no global state apart from the per-thread error text.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sparse_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *msg) {
+  snprintf(g_err, sizeof(g_err), "%s", msg);
+  return code;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Common checks of the mode parameters.  Returns SA_OK or an error code.
+int check_mode(int mode, int k_win, int pi, int M, int seg) {
+  if (mode == SA_MODE_ECP) {
+    if (seg <= 0) return fail(SA_ERR_INVALID, "ECP mode needs seg >= 1");
+    return SA_OK;
+  }
+  if (mode != SA_MODE_PI && mode != SA_MODE_WINDOW) return fail(SA_ERR_INVALID, "unknown mode");
+  if (k_win < 0) return fail(SA_ERR_INVALID, "k_win must be >= 0");
+  if (mode == SA_MODE_PI) {
+    if (M < 0) return fail(SA_ERR_INVALID, "M must be >= 0");
+    if (M > 0 && pi <= 0) return fail(SA_ERR_INVALID, "pi must be >= 1 when M > 0");
+  }
+  return SA_OK;
+}
+
+int check_shape(int dtype, int d) {
+  if (dtype != SA_DTYPE_F32 && dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  return SA_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == SA_DTYPE_BF16 ? 2 : 4; }
+
+// Smallest m with m*pi > k_win: the first skip offset lying below the window.
+long long skip_m_min(int k_win, int pi) { return (long long)k_win / pi + 1; }
+
+// True when some query of a length-N sequence has a skip key below its window.
+bool has_skips(int mode, int k_win, int pi, int M, int N) {
+  if (mode != SA_MODE_PI || M <= 0) return false;
+  const long long mm = skip_m_min(k_win, pi);
+  return mm <= M && mm * (long long)pi <= (long long)N - 1;
+}
+
+struct FwdLayout {
+  size_t ml_off, acc_off, total;
+};
+
+FwdLayout fwd_layout(int B, int Hq, int N, int d) {
+  FwdLayout L;
+  const size_t rows = (size_t)B * Hq * N;
+  L.ml_off = 0;
+  L.acc_off = round_up(rows * 2 * sizeof(float), 256);
+  L.total = L.acc_off + round_up(rows * (size_t)d * sizeof(float), 256);
+  return L;
+}
+
+int fwd_validate(const void *q, const void *k, const void *v, const float *alpha, void *o, int B, int Hq,
+                 int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg) {
+  int rc = check_shape(dtype, d);
+  if (rc != SA_OK) return rc;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and N must be >= 1");
+  if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
+  rc = check_mode(mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return fail(SA_ERR_INVALID, "null tensor pointer");
+  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 4))
+    return fail(SA_ERR_INVALID, "misaligned tensor (q/k/v/o need 16 bytes, alpha 4)");
+  const long long rows = (long long)B * Hq * N;
+  const long long blocks = (long long)B * Hq * ((N + sa::kPrefillBM - 1) / sa::kPrefillBM);
+  if (rows >= (1LL << 31) || blocks >= (1LL << 31) || (long long)N * d >= (1LL << 31))
+    return fail(SA_ERR_INVALID, "problem too large for 32-bit row indexing");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)rows * d * es, nkv = (size_t)B * Hkv * N * d * es;
+  const size_t na = (mode == SA_MODE_PI && alpha) ? (size_t)rows * sizeof(float) : 0;
+  if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) || overlap(o, nq, alpha, na))
+    return fail(SA_ERR_INVALID, "output overlaps an input");
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_attn_fwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win,
+                                      int pi, int M, int seg) {
+  if (check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || Hq % Hkv != 0 ||
+      check_mode(mode, k_win, pi, M, seg) != SA_OK)
+    return 0;
+  if (!has_skips(mode, k_win, pi, M, N)) return 0;
+  return fwd_layout(B, Hq, N, d).total;
+}
+
+int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *alpha, void *o, int B, int Hq,
+                    int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  int rc = fwd_validate(q, k, v, alpha, o, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  const bool skips = has_skips(mode, k_win, pi, M, N);
+  FwdLayout L = fwd_layout(B, Hq, N, d);
+  if (skips) {
+    if (workspace == nullptr || workspace_bytes < L.total)
+      return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_fwd_workspace_size()");
+    if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+    const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype);
+    if (overlap(o, nq, workspace, L.total)) return fail(SA_ERR_INVALID, "output overlaps the workspace");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  sa::PrefillArgs pa;
+  pa.q = q; pa.k = k; pa.v = v; pa.alpha = alpha; pa.o = o;
+  pa.skip_ml = nullptr; pa.skip_acc = nullptr;
+  pa.B = B; pa.Hq = Hq; pa.Hkv = Hkv; pa.N = N; pa.d = d; pa.dtype = dtype;
+  pa.mode = mode; pa.k_win = k_win; pa.seg = seg;
+  pa.skip_first = N;
+  if (skips) {
+    const long long mm = skip_m_min(k_win, pi);
+    sa::SkipArgs sk;
+    sk.q = q; sk.k = k; sk.v = v; sk.alpha = alpha;
+    sk.ml = (float *)((char *)workspace + L.ml_off);
+    sk.acc = (float *)((char *)workspace + L.acc_off);
+    sk.B = B; sk.Hq = Hq; sk.Hkv = Hkv; sk.N = N; sk.d = d; sk.dtype = dtype;
+    sk.pi = pi; sk.M = M; sk.m_min = (int)mm;
+    hipError_t e = sa::launch_skip(sk, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+    pa.skip_ml = sk.ml;
+    pa.skip_acc = sk.acc;
+    pa.skip_first = (int)(mm * pi);
+  }
+  hipError_t e = sa::launch_prefill(pa, s);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+  return SA_OK;
+}
+
+// Decode split plan: the window range (at most k_win+1 rows, 2*seg for ECP,
+// never more than Lmax) is cut into splits of about 256 rows (a multiple of 64,
+// the rows one pass of a 4-wave workgroup covers); skip keys get one more split.
+static void decode_plan(int Lmax, int mode, int k_win, int pi, int M, int seg, int *n_wsplit, int *chunk,
+                        int *has_skip, int *m_min) {
+  long long range = mode == SA_MODE_ECP ? 2LL * seg : (long long)k_win + 1;
+  if (range > Lmax) range = Lmax;
+  int n = (int)((range + 255) / 256);
+  if (n < 1) n = 1;
+  long long c = (range + n - 1) / n;
+  c = (c + 63) / 64 * 64;
+  *n_wsplit = n;
+  *chunk = (int)c;
+  *has_skip = has_skips(mode, k_win, pi, M, Lmax) ? 1 : 0;
+  *m_min = (mode == SA_MODE_PI && pi > 0) ? (int)(skip_m_min(k_win, pi) < (1LL << 30) ? skip_m_min(k_win, pi) : (1LL << 30)) : 1;
+}
+
+size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d, int dtype, int mode, int k_win,
+                                         int pi, int M, int seg) {
+  if (check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv != 0 ||
+      check_mode(mode, k_win, pi, M, seg) != SA_OK)
+    return 0;
+  int nw, chunk, hs, mm;
+  decode_plan(Lmax, mode, k_win, pi, M, seg, &nw, &chunk, &hs, &mm);
+  return round_up((size_t)B * Hq * (nw + hs) * (d + 2) * sizeof(float), 256);
+}
+
+int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,
+                       const float *alpha, void *o, int B, int Hq, int Hkv, int Lmax, int d, int dtype, int mode,
+                       int k_win, int pi, int M, int seg, void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  int rc = check_shape(dtype, d);
+  if (rc != SA_OK) return rc;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and Lmax must be >= 1");
+  if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
+  rc = check_mode(mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || o == nullptr)
+    return fail(SA_ERR_INVALID, "null tensor pointer");
+  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(alpha, 4) || !aligned(cache_lens, 4))
+    return fail(SA_ERR_INVALID, "misaligned tensor");
+  if ((long long)B * Hkv * Lmax >= (1LL << 31) || (long long)Lmax * d >= (1LL << 31) || B > 65535)
+    return fail(SA_ERR_INVALID, "problem too large");
+  const size_t need = sparse_attn_decode_workspace_size(B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi, M, seg);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_decode_workspace_size()");
+  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * d * es, nc = (size_t)B * Hkv * Lmax * d * es;
+  if (overlap(o, nq, q, nq) || overlap(o, nq, k_cache, nc) || overlap(o, nq, v_cache, nc) ||
+      overlap(o, nq, alpha, alpha ? (size_t)B * Hq * 4 : 0) || overlap(o, nq, cache_lens, (size_t)B * 4) ||
+      overlap(o, nq, workspace, need))
+    return fail(SA_ERR_INVALID, "output overlaps an input or the workspace");
+  sa::DecodeArgs da;
+  da.q = q; da.kc = k_cache; da.vc = v_cache; da.lens = cache_lens; da.alpha = alpha; da.o = o;
+  da.ws = (float *)workspace;
+  da.B = B; da.Hq = Hq; da.Hkv = Hkv; da.Lmax = Lmax; da.d = d; da.dtype = dtype;
+  da.mode = mode; da.k_win = k_win; da.pi = pi; da.M = M; da.seg = seg;
+  decode_plan(Lmax, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.has_skip, &da.m_min);
+  da.nsplit = da.n_wsplit + da.has_skip;
+  hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+  return SA_OK;
+}
+
+const char *sparse_attn_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_HIP: return "HIP error";
+    case SA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char *sparse_attn_last_error(void) { return g_err; }
+
+int sparse_attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libsparse_attn.
+//
+// Lane layouts used throughout (wave64, verified on gfx950):
+//   v_mfma_f32_32x32x16_bf16: A lane l holds A[l%32][8*(l/32)+s], s=0..7;
+//       B lane l holds B[8*(l/32)+s][l%32]; C lane l holds
+//       C[8*(j/4) + 4*(l/32) + j%4][l%32], j=0..15.
+//   v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8*(l/16)+s];
+//       B[8*(l/16)+s][l%16]; C lane l holds C[4*(l/16)+j][l%16], j=0..3.
+//   v_mfma_f32_16x16x16bf16_1k: A[l%16][4*(l/16)+s], B[4*(l/16)+s][l%16], s=0..3.
+//   v_mfma_f32_32x32x2f32 / 16x16x4f32: one fp32 per lane, k index = l/32 or l/16.
+//   ds_read_b64_tr_b16: inside each group of 16 lanes, lane t receives
+//       element (t%4) of the 4-element chunk addressed by lane 4*j + t/4, j=0..3.
+//       With lanes 4j..4j+3 pointing at row r_j, columns c0 + 4*(lane%4), lane t
+//       gets [row r_j][c0 + t] for j = 0..3: a transposed fragment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// Running-max sentinel: finite, so exp2(sentinel - x) is 0 and sentinel - sentinel is 0.
+constexpr float kNegBig = -1.0e30f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short u) {
+  return __uint_as_float(((unsigned int)u) << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (unsigned short)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// Two transposed 4-element reads joined into one 8-element MFMA operand.  Whole
+// vectors are reinterpreted (no per-element extraction).
+__device__ __forceinline__ bf16x8 join_bf16x8(short4v lo, short4v hi) {
+  const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x4 as_bf16x4(short4v x) { return __builtin_bit_cast(bf16x4, x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 x) {
+  return bf16_to_f32(__builtin_bit_cast(unsigned short, x));
+}
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// XCD-aware remap of a 1-D grid: hardware hands consecutive workgroup ids to the
+// 8 XCDs round-robin; this returns a logical id such that each XCD receives one
+// contiguous range of logical ids (neighbouring tiles share its L2).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = bid % 8, idx = bid / 8;
+  return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace sa

@@ -1,0 +1,52 @@
+// kernels.hpp -- host-side launch interface between the C ABI (api.hip) and the
+// gfx950 kernels.  Internal to libsparse_attn; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace sa {
+
+enum { kModePi = 0, kModeWindow = 1, kModeEcp = 2 };
+enum { kF32 = 0, kBF16 = 1 };
+
+// Prefill: query block of 128 rows per workgroup, key tiles of 64 rows.
+constexpr int kPrefillBM = 128;
+constexpr int kPrefillBN = 64;
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *alpha;   // [B,Hq,N] or nullptr (PI priors)
+  void *o;
+  const float *skip_ml; // [B*Hq*N][2] (running max in log2 units, sum) or nullptr
+  const float *skip_acc;// [B*Hq*N][d] unnormalised skip accumulators or nullptr
+  int B, Hq, Hkv, N, d, dtype;
+  int mode, k_win, seg;
+  int skip_first;       // first query position that has a skip key (PI), else N
+};
+
+struct SkipArgs {
+  const void *q, *k, *v;
+  const float *alpha;   // [B,Hq,N]
+  float *ml;            // [B*Hq*N][2]
+  float *acc;           // [B*Hq*N][d]
+  int B, Hq, Hkv, N, d, dtype;
+  int pi, M, m_min;     // skip offsets m*pi for m in [m_min, M]
+};
+
+struct DecodeArgs {
+  const void *q, *kc, *vc;
+  const int *lens;
+  const float *alpha;   // [B,Hq] or nullptr
+  void *o;
+  float *ws;            // [B*Hq][nsplit][d+2]
+  int B, Hq, Hkv, Lmax, d, dtype;
+  int mode, k_win, pi, M, seg, m_min;
+  int n_wsplit, chunk, has_skip, nsplit;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_skip(const SkipArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace sa

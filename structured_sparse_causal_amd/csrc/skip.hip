@@ -1,0 +1,214 @@
+// skip.hip -- periodic skip keys of pi-Attention as a residue-class pass (gfx950).
+//
+// pi-Attention (section 2, item 2) lets query i attend i - m*pi for m = 1..M;
+// the keys that lie below the causal window [i-k, i] are those with
+// m*pi > k, i.e. m >= m_min = floor(k/pi) + 1.  Query i and its skip keys share
+// the residue r = i mod pi: within one residue class, queries at periods
+// p = (i - r)/pi attend the earlier periods p - m.  For a fixed residue this is
+// a small dense band problem, so a wave gathers (strided gather, section 2
+// item 2) 16 query periods and 16 key periods of one residue and runs it on
+// the matrix cores: S^T = K Q^T with v_mfma_f32_16x16x32_bf16, band mask
+// m in [m_min, M], log-prior log(1 - alpha_i) (item 3), then O^T = V^T P^T with
+// v_mfma_f32_16x16x16bf16_1k.  The pass writes, per query with at least one
+// skip key, the partial softmax state (running max in log2 units, sum,
+// unnormalised accumulator); the prefill kernel starts from it, so the union
+// of local and skip keys gets a single softmax.
+//
+// The fp32 I/O variant (small, correctness-first inputs) uses a plain per-query
+// loop on the vector ALUs.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sa {
+namespace {
+
+struct Params {
+  const void *q, *k, *v;
+  const float *alpha;
+  float *ml, *acc;
+  int N, Hq, Hkv, pi, M, m_min;
+  int P;          // periods per residue: ceil(N / pi)
+  int ntiles;     // query-period tiles of 16 per residue
+  int nwork;      // B*Hq*pi*ntiles work items (one per wave)
+  float scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
+  constexpr int LD = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Vs[4][16 * LD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int work = blockIdx.x * 4 + wave;
+  if (work >= p.nwork) return;  // no block-level barrier below: waves are independent
+  const int tile = work % p.ntiles;
+  const int r = (work / p.ntiles) % p.pi;
+  const int bh = work / (p.ntiles * p.pi);
+  const int hq = bh % p.Hq, b = bh / p.Hq, g = hq / (p.Hq / p.Hkv);
+  const int N = p.N;
+  const int G = lane >> 4, t = lane & 15;
+  const int p0 = p.m_min + 16 * tile;         // first query period of this tile
+  const int pq = p0 + t;                       // query period of lane column t
+  const int iq = r + pq * p.pi;                // its position
+  const bool qvalid = pq < p.P && iq < N;
+
+  const bf16 *Qp = (const bf16 *)p.q + (size_t)bh * N * D;
+  const bf16 *Kp = (const bf16 *)p.k + (size_t)(b * p.Hkv + g) * N * D;
+  const bf16 *Vp = (const bf16 *)p.v + (size_t)(b * p.Hkv + g) * N * D;
+
+  bf16x8 qf[D / 32];
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qf[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
+  float bias = -INFINITY;  // log2(1 - alpha)
+  if (qvalid) bias = __log2f(1.0f - p.alpha[(size_t)bh * N + iq]);
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
+  float m_run = kNegBig, l_run = 0.f;
+  bf16 *vs = Vs[wave];
+
+  const int kt_lo = max(0, p0 - p.M);
+  const int kt_hi = p0 + 15 - p.m_min;
+  for (int kt = kt_lo; kt <= kt_hi; kt += 16) {
+    // Key periods kt + 4G + jj (score rows), kt + t (operand rows).
+    const int pk = kt + t;
+    const int ik = r + pk * p.pi;
+    const bool kvalid = pk < p.P && ik < N;
+    f32x4 s = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const bf16x8 a = kvalid ? *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], s, 0, 0, 0);
+    }
+    // Stage the 16 value rows of this key tile in this wave's LDS slab.
+#pragma unroll
+    for (int ci = lane; ci < 16 * D / 8; ci += 64) {
+      const int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int pr = kt + row, ir = r + pr * p.pi;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (pr < p.P && ir < N) vv = *(const uint4 *)(Vp + (size_t)ir * D + col);
+      *(uint4 *)(vs + row * LD + col) = vv;
+    }
+    // Band mask: key period pk' = kt + 4G + jj is a skip key of query period pq
+    // iff m = pq - pk' lies in [m_min, M].
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int m = pq - (kt + 4 * G + jj);
+      const bool ok = qvalid && m >= p.m_min && m <= p.M;
+      s[jj] = ok ? s[jj] * p.scale_log2 + bias : -INFINITY;
+      mx = fmaxf(mx, s[jj]);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float mr = fmaxf(m_run, mx);
+    const float f = fast_exp2(m_run - mr);
+    l_run *= f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) acc[db] *= f;
+    m_run = mr;
+    bf16x4 pb;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float pv = fast_exp2(s[jj] - m_run);
+      l_run += pv;
+      pb[jj] = (bf16)pv;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += V^T P^T over the 16 key periods (K = 16).
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const bf16 *src = vs + (4 * G + (t >> 2)) * LD + 16 * db + 4 * (t & 3);
+      const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src);
+      const bf16x4 a = as_bf16x4(x);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  l_run += wave_shfl_xor(l_run, 16);
+  l_run += wave_shfl_xor(l_run, 32);
+  if (!qvalid) return;
+  const size_t row = (size_t)bh * N + iq;
+  if (G == 0) {
+    p.ml[2 * row] = m_run;
+    p.ml[2 * row + 1] = l_run;
+  }
+  float *ap = p.acc + row * D;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) *(f32x4 *)(ap + 16 * db + 4 * G) = acc[db];
+}
+
+// fp32 I/O: one thread per query row, plain loops.
+template <int D>
+__global__ __launch_bounds__(128) void skip_f32_kernel(Params p, int first, long long rows) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows) return;
+  const int per_head = p.N - first;
+  const int bh = (int)(idx / per_head);
+  const int i = first + (int)(idx % per_head);
+  const int hq = bh % p.Hq, b = bh / p.Hq, g = hq / (p.Hq / p.Hkv);
+  const float *Qp = (const float *)p.q + ((size_t)bh * p.N + i) * D;
+  const float *Kp = (const float *)p.k + (size_t)(b * p.Hkv + g) * p.N * D;
+  const float *Vp = (const float *)p.v + (size_t)(b * p.Hkv + g) * p.N * D;
+  const float bias = __log2f(1.0f - p.alpha[(size_t)bh * p.N + i]);
+  float acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) acc[c] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+  for (int m = p.m_min; m <= p.M; ++m) {
+    const int j = i - m * p.pi;
+    if (j < 0) break;
+    float dot = 0.f;
+    for (int c = 0; c < D; ++c) dot = fmaf(Qp[c], Kp[(size_t)j * D + c], dot);
+    const float sc = dot * p.scale_log2 + bias;
+    const float mr = fmaxf(m_run, sc);
+    const float f = fast_exp2(m_run - mr);
+    const float pv = fast_exp2(sc - mr);
+    l_run = l_run * f + pv;
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[c] = acc[c] * f + pv * Vp[(size_t)j * D + c];
+    m_run = mr;
+  }
+  const size_t row = (size_t)bh * p.N + i;
+  p.ml[2 * row] = m_run;
+  p.ml[2 * row + 1] = l_run;
+#pragma unroll
+  for (int c = 0; c < D; ++c) p.acc[row * D + c] = acc[c];
+}
+
+template <int D>
+hipError_t launch_t(const SkipArgs &a, hipStream_t s) {
+  Params p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.ml = a.ml; p.acc = a.acc;
+  p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.pi = a.pi; p.M = a.M; p.m_min = a.m_min;
+  p.P = (a.N + a.pi - 1) / a.pi;
+  p.scale_log2 = kLog2e / sqrtf((float)D);
+  const int first = a.m_min * a.pi;  // first position with a skip key
+  if (first >= a.N) return hipSuccess;
+  if (a.dtype == kBF16) {
+    p.ntiles = (p.P - a.m_min + 15) / 16;
+    const long long nwork = (long long)a.B * a.Hq * a.pi * p.ntiles;
+    p.nwork = (int)nwork;
+    hipLaunchKernelGGL((skip_bf16_kernel<D>), dim3((p.nwork + 3) / 4), dim3(256), 0, s, p);
+  } else {
+    p.ntiles = 0;
+    p.nwork = 0;
+    const long long rows = (long long)a.B * a.Hq * (a.N - first);
+    hipLaunchKernelGGL((skip_f32_kernel<D>), dim3((unsigned)((rows + 127) / 128)), dim3(128), 0, s, p,
+                       first, rows);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_skip(const SkipArgs &a, hipStream_t s) {
+  return a.d == 64 ? launch_t<64>(a, s) : launch_t<128>(a, s);
+}
+
+}  // namespace sa

@@ -1,0 +1,127 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+rejects bad arguments on the host before any HIP call (CPU only: every call
+here fails validation, so no kernel is launched and no device is touched)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from structured_sparse_causal_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+SA_OK, INVALID, UNSUPPORTED, HIP, WORKSPACE = 0, -1, -2, -3, -4
+PI, WINDOW, ECP = 0, 1, 2
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sparse_attn_version() == 100
+    assert lib.sparse_attn_status_string(SA_OK) == b"ok"
+    assert lib.sparse_attn_status_string(WORKSPACE) == b"workspace too small"
+    assert lib.sparse_attn_status_string(12345) == b"unknown status"
+
+
+# Fake, never-dereferenced device addresses (validation fails before use).
+Q, K, V, A, O, WS = (0x100000 * (i + 1) for i in range(6))
+
+
+def fwd(lib, q=Q, k=K, v=V, a=A, o=O, B=1, Hq=2, Hkv=2, N=256, d=64, dtype=BF16, mode=PI,
+        k_win=32, pi=64, M=3, seg=0, ws=None, wsb=0):
+    return lib.sparse_attn_fwd(q, k, v, a, o, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg,
+                               ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(Hq=3, Hkv=2), INVALID),
+    (dict(mode=5), INVALID), (dict(k_win=-1), INVALID), (dict(M=-1), INVALID),
+    (dict(pi=0), INVALID), (dict(mode=ECP, seg=0), INVALID), (dict(q=None), INVALID),
+    (dict(o=None), INVALID), (dict(a=None), INVALID), (dict(q=Q + 8), INVALID),
+    (dict(a=A + 2), INVALID), (dict(o=Q), INVALID), (dict(o=K + 64), INVALID),
+    (dict(), WORKSPACE), (dict(ws=WS, wsb=16), WORKSPACE),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.sparse_attn_last_error() != b""
+
+
+def test_fwd_alpha_optional_without_skips(lib):
+    # WINDOW and ECP ignore alpha; validation must not demand it.  Use an
+    # overlapping output so the call still fails before any launch.
+    assert fwd(lib, a=None, mode=WINDOW, o=Q) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+    assert fwd(lib, a=None, mode=ECP, seg=64, o=Q) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+
+
+def test_fwd_workspace_sizes(lib):
+    ws = lib.sparse_attn_fwd_workspace_size
+    # pi-Attention with skip keys: (m, l) pairs plus a d-wide fp32 accumulator per row.
+    rows = 2 * 16 * 16384
+    assert ws(2, 16, 16, 16384, 64, BF16, PI, 256, 1024, 15, 0) == rows * 8 + rows * 64 * 4
+    assert ws(1, 32, 32, 65536, 128, BF16, WINDOW, 1024, 0, 0, 0) == 0
+    assert ws(4, 12, 12, 4096, 64, BF16, ECP, 0, 0, 0, 512) == 0
+    assert ws(1, 2, 2, 256, 64, F32, PI, 32, 64, 0, 0) == 0          # M = 0
+    assert ws(1, 2, 2, 256, 64, F32, PI, 300, 64, 4, 0) == 0         # every skip inside the window
+    assert ws(1, 2, 2, 100, 64, F32, PI, 32, 64, 3, 0) > 0           # position 64 has key 0
+    assert ws(1, 2, 2, 64, 64, F32, PI, 32, 64, 3, 0) == 0           # no position reaches a skip
+    assert ws(1, 2, 2, 256, 96, F32, PI, 32, 64, 3, 0) == 0          # rejected arguments
+
+
+def dec(lib, q=Q, kc=K, vc=V, lens=A, a=A + 4096, o=O, B=2, Hq=8, Hkv=2, L=512, d=128, dtype=BF16,
+        mode=PI, k_win=64, pi=64, M=3, seg=0, ws=WS, wsb=1 << 30):
+    return lib.sparse_attn_decode(q, kc, vc, lens, a, o, B, Hq, Hkv, L, d, dtype, mode, k_win, pi, M,
+                                  seg, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=80), UNSUPPORTED), (dict(Hq=6, Hkv=4), INVALID), (dict(L=0), INVALID),
+    (dict(lens=None), INVALID), (dict(a=None), INVALID), (dict(mode=ECP, seg=-3), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(ws=WS + 64), INVALID),
+    (dict(o=K + 128), INVALID), (dict(o=WS), INVALID), (dict(lens=A + 2), INVALID),
+])
+def test_decode_rejects(lib, kw, code):
+    assert dec(lib, **kw) == code
+
+
+def test_decode_workspace_size(lib):
+    ws = lib.sparse_attn_decode_workspace_size
+    # 2049 window rows -> 9 splits of 256, plus one split for the skip keys.
+    assert ws(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0) == 64 * 32 * 10 * 130 * 4
+    assert ws(64, 32, 8, 32768, 128, BF16, WINDOW, 2048, 0, 0, 0) == 64 * 32 * 9 * 130 * 4
+    assert ws(1, 1, 1, 100, 64, F32, ECP, 0, 0, 0, 512) == 256 * ((1 * 1 * 1 * 66 * 4 + 255) // 256)
+    assert ws(1, 1, 1, 100, 60, F32, ECP, 0, 0, 0, 512) == 0
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q, q, mode="window", k_win=2)
