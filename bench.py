@@ -1,0 +1,318 @@
+"""Benchmark of the causal structured-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One "step" is one forward of the headline workload (default: ECP
+paired-half-segment attention, bf16, B=4 H=12 N=4096 d=64 s=512) on synthetic
+inputs already resident in HBM.  ``value`` is useful TFLOP/s: 4*d FLOPs per
+attended (query, key) pair, nothing for masked or padded work.  The same JSON
+line carries the roofline of the dominant kernel (timed live with HIP events
+on the launch stream), the other workloads of the hot path (pi-Attention
+prefill, the looped window block, GQA decode) and the CPU oracle timed on a
+bounded sample of the headline workload.
+
+Only one GPU is used; ``--gpus N`` with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 (published)
+MFMA_F32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
+METRIC = "useful TFLOP/s + % bf16 MFMA peak (prefill); decode HBM GB/s (1 GPU)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Useful work (attended pairs) and algorithmic bytes, from the mask definitions
+# ---------------------------------------------------------------------------
+def key_lo(i, w):
+    if w.mode == "ecp":
+        return np.maximum(0, (i // w.seg - 1) * w.seg)
+    return np.maximum(0, i - w.k_win)
+
+
+def pairs_per_head(w, N=None):
+    """Attended (query, key) pairs of one (batch, head): window or ECP range
+    plus, for pi-Attention, the skip keys lying below the window."""
+    N = w.N if N is None else N
+    i = np.arange(N, dtype=np.int64)
+    n = (i - key_lo(i, w) + 1).sum()
+    if w.mode == "pi" and w.M > 0:
+        lo = key_lo(i, w)
+        for m in range(1, w.M + 1):
+            j = i - m * w.pi
+            n += int(((j >= 0) & (j < lo)).sum())
+    return int(n)
+
+
+def decode_keys(w, L):
+    i = L - 1
+    lo = int(key_lo(np.array([i]), w)[0])
+    n = i - lo + 1
+    if w.mode == "pi":
+        n += sum(1 for m in range(1, w.M + 1) if 0 <= i - m * w.pi < lo)
+    return n
+
+
+def prefill_useful(w):
+    flop = 4.0 * w.d * pairs_per_head(w) * w.B * w.Hq
+    es = 2 if w.dtype == "bf16" else 4
+    nbytes = es * w.d * w.N * (2 * w.B * w.Hq + 2 * w.B * w.Hkv)
+    if w.mode == "pi":
+        nbytes += 4 * w.B * w.Hq * w.N
+    return flop, float(nbytes)
+
+
+def decode_useful(w):
+    keys = decode_keys(w, w.N)
+    es = 2 if w.dtype == "bf16" else 4
+    rows = w.B * w.Hkv * keys
+    nbytes = 2 * rows * w.d * es + 2 * w.B * w.Hq * w.d * es + 4 * w.B
+    if w.mode == "pi":
+        nbytes += 4 * w.B * w.Hq
+    flop = 4.0 * w.d * keys * w.B * w.Hq
+    return flop, float(nbytes)
+
+
+# ---------------------------------------------------------------------------
+# Timing helpers
+# ---------------------------------------------------------------------------
+def event_times(torch, fn, reps):
+    """Per-call GPU durations (ms) from HIP events recorded on the current
+    stream, the stream the library launches on."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def run_prefill_workload(torch, sa, w, reps, warmup):
+    from structured_sparse_causal_amd.inputs import prefill_inputs
+    dev = torch.device("cuda:0")
+    q, k, v, a = prefill_inputs(w, device=dev)
+    prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+    outs = (torch.empty_like(q), torch.empty_like(q))
+    nbytes = sa.fwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, q.dtype, w.mode, w.k_win, w.pi,
+                                   w.M, w.seg)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if w.loops > 1:
+        def fn():
+            sa.loop_fwd(q, k, v, a, steps=w.loops, outs=outs, workspace=ws, **prm)
+    else:
+        def fn():
+            sa.fwd(q, k, v, a, out=outs[0], workspace=ws, **prm)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t = event_times(torch, fn, reps)
+    flop, nb = prefill_useful(w)
+    flop *= w.loops
+    nb *= w.loops
+    ms = float(np.median(t))
+    ai = flop / nb
+    attainable = min(MFMA_BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1000.0)
+    res = {
+        "ms": ms, "ms_p10": float(np.percentile(t, 10)), "ms_p90": float(np.percentile(t, 90)),
+        "useful_tflops": flop / (ms * 1e-3) / 1e12,
+        "pct_bf16_mfma_peak": 100.0 * flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "arith_intensity": ai, "attainable_tflops": attainable,
+        "pct_attainable": 100.0 * flop / (ms * 1e-3) / 1e12 / attainable,
+        "useful_flop": flop, "useful_bytes": nb, "launches": w.loops * (2 if nbytes else 1),
+    }
+    del q, k, v, a, outs, ws
+    return res
+
+
+def run_decode_workload(torch, sa, w, reps, warmup):
+    from structured_sparse_causal_amd.inputs import decode_inputs
+    dev = torch.device("cuda:0")
+    q, kc, vc, lens, a = decode_inputs(w, device=dev)
+    out = torch.empty_like(q)
+    nbytes = sa.decode_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, q.dtype, w.mode, w.k_win, w.pi,
+                                      w.M, w.seg)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def fn():
+        sa.decode(q, kc, vc, lens, a, mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg,
+                  out=out, workspace=ws)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t = event_times(torch, fn, reps)
+    flop, nb = decode_useful(w)
+    ms = float(np.median(t))
+    res = {
+        "ms": ms, "ms_p10": float(np.percentile(t, 10)), "ms_p90": float(np.percentile(t, 90)),
+        "useful_GBps": nb / (ms * 1e-3) / 1e9,
+        "pct_hbm_peak": 100.0 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tokens_per_s": w.B / (ms * 1e-3), "useful_bytes": nb, "useful_flop": flop,
+    }
+    del q, kc, vc, lens, a, out, ws
+    return res
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle (fp64, OpenMP over query rows) on a bounded sample of the
+    workload: whole (batch, head) slices, grown until about budget_s of CPU
+    work; reported in the headline unit (useful TFLOP/s)."""
+    import oracle
+    from structured_sparse_causal_amd.inputs import prefill_inputs
+    q, k, v, a = prefill_inputs(w)
+    per_head_flop = 4.0 * w.d * pairs_per_head(w)
+    nthreads = oracle.num_threads()
+
+    def run(nh):
+        heads = [(b, h) for b in range(w.B) for h in range(w.Hq)][:nh]
+        rows = np.concatenate([(np.int64(b * w.Hq + h) * w.N + np.arange(w.N)) for b, h in heads])
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, a, mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg, rows=rows)
+        return time.perf_counter() - t0
+
+    nh, dt = 1, run(1)
+    total = w.B * w.Hq
+    if dt < budget_s and nh < total:
+        nh = int(min(total, max(1, math.floor(budget_s / max(dt, 1e-3)))))
+        dt = run(nh)
+    flop = per_head_flop * nh
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices of %s, all %d query rows each, fp64 C oracle; "
+                      "%.2f s" % (nh, total, w.name, w.N, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ecp_bf16")
+    ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (one MI355X per box); "
+              "--gpus %d is not supported. Run with --gpus 1." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structured_sparse_causal_amd as sa
+    from structured_sparse_causal_amd.inputs import WORKLOADS, prefill_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sa.load_library()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    if w.decode:
+        raise SystemExit("the headline workload must be a prefill workload")
+    log("bench: headline %s" % (w,))
+
+    # ---- headline: K timed steps bracketed by synchronisation ---------------
+    q, k, v, a = prefill_inputs(w, device=dev)
+    prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+    out = torch.empty_like(q)
+    outs = (out, torch.empty_like(q))
+    nbytes = sa.fwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, q.dtype, w.mode, w.k_win, w.pi,
+                                   w.M, w.seg)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        if w.loops > 1:
+            sa.loop_fwd(q, k, v, a, steps=w.loops, outs=outs, workspace=ws, **prm)
+        else:
+            sa.fwd(q, k, v, a, out=out, workspace=ws, **prm)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    flop, nb = prefill_useful(w)
+    flop_step = flop * w.loops
+    value = flop_step / (wall / args.steps) / 1e12
+
+    # Dominant kernel: per-launch durations from HIP events on the launch stream.
+    t_ev = event_times(torch, step, args.steps)
+    kern_ms = float(np.mean(t_ev)) / (w.loops if w.loops > 1 else 1)
+    dominant = "prefill_kernel<bf16,%d>" % w.d
+    achieved = flop / (kern_ms * 1e-3) / 1e12
+    ai = flop / nb
+    bound = "mfma" if ai * HBM_PEAK_GBS / 1000.0 >= MFMA_BF16_PEAK_TFLOPS else "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        gbs = nb / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    roof["kernel"] = dominant
+    roof["kernel_ms"] = kern_ms
+    roof["algorithmic_flop_per_launch"] = flop
+    roof["algorithmic_bytes_per_launch"] = nb
+    log("headline: %.4f ms/step, %.1f useful TFLOP/s (events: %.4f ms/launch)" % (
+        ms_step, value, kern_ms))
+    del q, k, v, a, out, outs, ws
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads of the hot path --------------------------------
+    extras = {}
+    if not args.no_extras:
+        for name in ("pi_tiny_f32", "ecp_bf16", "pi_bf16", "window_loop_bf16", "decode_pi_gqa_bf16"):
+            wx = WORKLOADS[name]
+            log("bench: workload %s" % name)
+            reps = 10 if name == "window_loop_bf16" else 30
+            if wx.decode:
+                extras[name] = run_decode_workload(torch, sa, wx, reps, 3)
+            else:
+                extras[name] = run_prefill_workload(torch, sa, wx, reps, 3)
+            log("  %s" % json.dumps(extras[name]))
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(w)
+        log("  %s" % json.dumps(cpu))
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "k_win": w.k_win, "pi": w.pi, "M": w.M, "seg": w.seg,
+                   "loops": w.loops, "parallelism": "none (1 GPU)"},
+        "pct_bf16_mfma_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": extras,
+        "gpu": torch.cuda.get_device_properties(0).gcnArchName,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
