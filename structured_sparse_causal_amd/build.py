@@ -31,6 +31,10 @@ def flags() -> list:
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             # no packed-fp32 instructions in any generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in ordinary VGPRs: the softmax reads every
+            # score and rescales the output accumulator, so AGPR homes would
+            # cost a copy per value per tile
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             "-Wno-unused-command-line-argument"]
 
