@@ -92,7 +92,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
   const int logical = xcd_remap(blockIdx.x, p.total);
-  const int qb = logical % p.nqb, bh = logical / p.nqb;
+  // Within a head the blocks run last-to-first: late blocks have the longest
+  // key ranges (ECP, causal edges), so the light ones form the grid's tail.
+  const int qb = p.nqb - 1 - logical % p.nqb, bh = logical / p.nqb;
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int g = hq / (p.Hq / p.Hkv);
   const int N = p.N;
