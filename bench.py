@@ -37,6 +37,56 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("structured_sparse_causal_amd/csrc/prefill.hip",
+                  "structured_sparse_causal_amd/csrc/common.hpp")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources of the dominant (prefill) kernel: a recorded
+    counter measurement is only reused while this hash is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the rocprofv3 counter
+    summary committed under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
+    by the reading of a plain copy of known size).  None if there is no
+    summary for this workload or the kernel changed since it was taken."""
+    path = os.path.join(PROFILES, "counters_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith("- "):
+                k, v = line.strip()[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: %d copies of %d bytes" % (reps, nbytes))
+
+
 # ---------------------------------------------------------------------------
 # Useful work (attended pairs) and algorithmic bytes, from the mask definitions
 # ---------------------------------------------------------------------------
@@ -207,6 +257,8 @@ def main():
     ap.add_argument("--workload", default="ecp_bf16")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (one MI355X per box); "
@@ -220,6 +272,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     sa.load_library()
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
@@ -269,6 +324,8 @@ def main():
         gbs = nb / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    traffic = recorded_traffic(w.name)
+    roof["traffic"] = traffic
     roof["kernel"] = dominant
     roof["kernel_ms"] = kern_ms
     roof["algorithmic_flop_per_launch"] = flop
