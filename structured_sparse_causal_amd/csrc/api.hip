@@ -61,16 +61,35 @@ bool has_skips(int mode, int k_win, int pi, int M, int N) {
   return mm <= M && mm * (long long)pi <= (long long)N - 1;
 }
 
+// pi-Attention with skip keys runs as (skip pass, prefill) pairs over chunks of
+// whole GQA groups of (batch, head) slices.  The workspace holds one chunk's
+// skip state (an (m, l) pair and a d-wide accumulator per query row) and is
+// capped at kChunkBytes, so it stays resident in the 256 MB last-level cache
+// between the two launches and does not grow with B * Hq.  Chunks are
+// balanced: a short last chunk would leave most of the GPU idle.
+constexpr size_t kChunkBytes = (size_t)128 << 20;
+
+int fwd_chunk_heads(int B, int Hq, int Hkv, int N, int d, int dtype) {
+  const int grp = Hq / Hkv;
+  const size_t per_group = (size_t)grp * N * (2 * sizeof(float) + (size_t)d * elem_size(dtype));
+  size_t fit = kChunkBytes / per_group;
+  if (fit < 1) fit = 1;
+  const size_t total_groups = (size_t)B * Hkv;
+  const size_t nchunks = (total_groups + fit - 1) / fit;
+  const size_t groups = (total_groups + nchunks - 1) / nchunks;
+  return (int)(groups * grp);
+}
+
 struct FwdLayout {
   size_t ml_off, acc_off, total;
 };
 
-FwdLayout fwd_layout(int B, int Hq, int N, int d) {
+FwdLayout fwd_layout(int heads, int N, int d, int dtype) {
   FwdLayout L;
-  const size_t rows = (size_t)B * Hq * N;
+  const size_t rows = (size_t)heads * N;
   L.ml_off = 0;
   L.acc_off = round_up(rows * 2 * sizeof(float), 256);
-  L.total = L.acc_off + round_up(rows * (size_t)d * sizeof(float), 256);
+  L.total = L.acc_off + round_up(rows * (size_t)d * elem_size(dtype), 256);
   return L;
 }
 
@@ -108,7 +127,7 @@ size_t sparse_attn_fwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int 
       check_mode(mode, k_win, pi, M, seg) != SA_OK)
     return 0;
   if (!has_skips(mode, k_win, pi, M, N)) return 0;
-  return fwd_layout(B, Hq, N, d).total;
+  return fwd_layout(fwd_chunk_heads(B, Hq, Hkv, N, d, dtype), N, d, dtype).total;
 }
 
 int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *alpha, void *o, int B, int Hq,
@@ -118,14 +137,6 @@ int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *al
   int rc = fwd_validate(q, k, v, alpha, o, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
   if (rc != SA_OK) return rc;
   const bool skips = has_skips(mode, k_win, pi, M, N);
-  FwdLayout L = fwd_layout(B, Hq, N, d);
-  if (skips) {
-    if (workspace == nullptr || workspace_bytes < L.total)
-      return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_fwd_workspace_size()");
-    if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
-    const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype);
-    if (overlap(o, nq, workspace, L.total)) return fail(SA_ERR_INVALID, "output overlaps the workspace");
-  }
   hipStream_t s = (hipStream_t)stream;
   sa::PrefillArgs pa;
   pa.q = q; pa.k = k; pa.v = v; pa.alpha = alpha; pa.o = o;
@@ -133,22 +144,47 @@ int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *al
   pa.B = B; pa.Hq = Hq; pa.Hkv = Hkv; pa.N = N; pa.d = d; pa.dtype = dtype;
   pa.mode = mode; pa.k_win = k_win; pa.seg = seg;
   pa.skip_first = N;
-  if (skips) {
-    const long long mm = skip_m_min(k_win, pi);
+  if (!skips) {
+    hipError_t e = sa::launch_prefill(pa, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+    return SA_OK;
+  }
+  const int chunk = fwd_chunk_heads(B, Hq, Hkv, N, d, dtype);
+  const FwdLayout L = fwd_layout(chunk, N, d, dtype);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_fwd_workspace_size()");
+  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * N * d * es;
+  if (overlap(o, nq, workspace, L.total)) return fail(SA_ERR_INVALID, "output overlaps the workspace");
+  const long long mm = skip_m_min(k_win, pi);
+  const int grp = Hq / Hkv;
+  const size_t head_elems = (size_t)N * d;
+  // A chunk of whole GQA groups is a contiguous range of (batch, head) slices;
+  // the kernels see it as one batch of `n` query heads and n/grp KV heads.
+  for (int bh0 = 0; bh0 < B * Hq; bh0 += chunk) {
+    const int n = B * Hq - bh0 < chunk ? B * Hq - bh0 : chunk;
     sa::SkipArgs sk;
-    sk.q = q; sk.k = k; sk.v = v; sk.alpha = alpha;
+    sk.q = (const char *)q + (size_t)bh0 * head_elems * es;
+    sk.k = (const char *)k + (size_t)(bh0 / grp) * head_elems * es;
+    sk.v = (const char *)v + (size_t)(bh0 / grp) * head_elems * es;
+    sk.alpha = alpha + (size_t)bh0 * N;
     sk.ml = (float *)((char *)workspace + L.ml_off);
-    sk.acc = (float *)((char *)workspace + L.acc_off);
-    sk.B = B; sk.Hq = Hq; sk.Hkv = Hkv; sk.N = N; sk.d = d; sk.dtype = dtype;
+    sk.acc = (char *)workspace + L.acc_off;
+    sk.B = 1; sk.Hq = n; sk.Hkv = n / grp; sk.N = N; sk.d = d; sk.dtype = dtype;
     sk.pi = pi; sk.M = M; sk.m_min = (int)mm;
     hipError_t e = sa::launch_skip(sk, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
-    pa.skip_ml = sk.ml;
-    pa.skip_acc = sk.acc;
-    pa.skip_first = (int)(mm * pi);
+    sa::PrefillArgs pc = pa;
+    pc.q = sk.q; pc.k = sk.k; pc.v = sk.v; pc.alpha = sk.alpha;
+    pc.o = (char *)o + (size_t)bh0 * head_elems * es;
+    pc.B = 1; pc.Hq = n; pc.Hkv = n / grp;
+    pc.skip_ml = sk.ml;
+    pc.skip_acc = sk.acc;
+    pc.skip_first = (int)(mm * pi);
+    e = sa::launch_prefill(pc, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   }
-  hipError_t e = sa::launch_prefill(pa, s);
-  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   return SA_OK;
 }
 

@@ -19,7 +19,7 @@ struct PrefillArgs {
   const float *alpha;   // [B,Hq,N] or nullptr (PI priors)
   void *o;
   const float *skip_ml; // [B*Hq*N][2] (running max in log2 units, sum) or nullptr
-  const float *skip_acc;// [B*Hq*N][d] unnormalised skip accumulators or nullptr
+  const void *skip_acc; // [B*Hq*N][d] unnormalised skip accumulators (I/O dtype) or nullptr
   int B, Hq, Hkv, N, d, dtype;
   int mode, k_win, seg;
   int skip_first;       // first query position that has a skip key (PI), else N
@@ -29,7 +29,7 @@ struct SkipArgs {
   const void *q, *k, *v;
   const float *alpha;   // [B,Hq,N]
   float *ml;            // [B*Hq*N][2]
-  float *acc;           // [B*Hq*N][d]
+  void *acc;            // [B*Hq*N][d] in the I/O dtype
   int B, Hq, Hkv, N, d, dtype;
   int pi, M, m_min;     // skip offsets m*pi for m in [m_min, M]
 };

@@ -40,7 +40,8 @@ struct Params {
   const void *q, *k, *v;
   const float *alpha;
   void *o;
-  const float *skip_ml, *skip_acc;
+  const float *skip_ml;
+  const void *skip_acc;
   int N, Hq, Hkv, mode, k_win, seg, nqb, total, skip_first;
   float scale_log2;
 };
@@ -134,14 +135,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
     const size_t row = (size_t)bh * N + qi;
     m_run = p.skip_ml[2 * row];
     if (h == 0) l_run = p.skip_ml[2 * row + 1];
-    const float *ap = p.skip_acc + row * D;
+    const T *ap = (const T *)p.skip_acc + row * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 x = *(const f32x4 *)(ap + 32 * db + 8 * j4 + 4 * h);
+        const T *src = ap + 32 * db + 8 * j4 + 4 * h;
+        if constexpr (kBF) {
+          const ushort4 u = *(const ushort4 *)src;
+          acc[db][4 * j4 + 0] = bf16_to_f32(u.x);
+          acc[db][4 * j4 + 1] = bf16_to_f32(u.y);
+          acc[db][4 * j4 + 2] = bf16_to_f32(u.z);
+          acc[db][4 * j4 + 3] = bf16_to_f32(u.w);
+        } else {
+          const f32x4 x = *(const f32x4 *)src;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[db][4 * j4 + e] = x[e];
+          for (int e = 0; e < 4; ++e) acc[db][4 * j4 + e] = x[e];
+        }
       }
   }
 

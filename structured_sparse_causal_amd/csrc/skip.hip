@@ -25,7 +25,8 @@ namespace {
 struct Params {
   const void *q, *k, *v;
   const float *alpha;
-  float *ml, *acc;
+  float *ml;
+  void *acc;
   int N, Hq, Hkv, pi, M, m_min;
   int P;          // periods per residue: ceil(N / pi)
   int ntiles;     // query-period tiles of 16 per residue
@@ -138,9 +139,18 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
     p.ml[2 * row] = m_run;
     p.ml[2 * row + 1] = l_run;
   }
-  float *ap = p.acc + row * D;
+  // Accumulators are stored in bf16 (the I/O precision): half the workspace
+  // traffic; the relative rounding (2^-9) applies to the skip share only.
+  bf16 *ap = (bf16 *)p.acc + row * D;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) *(f32x4 *)(ap + 16 * db + 4 * G) = acc[db];
+  for (int db = 0; db < D / 16; ++db) {
+    ushort4 u;
+    u.x = f32_to_bf16_bits(acc[db][0]);
+    u.y = f32_to_bf16_bits(acc[db][1]);
+    u.z = f32_to_bf16_bits(acc[db][2]);
+    u.w = f32_to_bf16_bits(acc[db][3]);
+    *(ushort4 *)(ap + 16 * db + 4 * G) = u;
+  }
 }
 
 // fp32 I/O: one thread per query row, plain loops.
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(128) void skip_f32_kernel(Params p, int first, long
   p.ml[2 * row] = m_run;
   p.ml[2 * row + 1] = l_run;
 #pragma unroll
-  for (int c = 0; c < D; ++c) p.acc[row * D + c] = acc[c];
+  for (int c = 0; c < D; ++c) ((float *)p.acc)[row * D + c] = acc[c];
 }
 
 template <int D>

@@ -83,9 +83,16 @@ def test_fwd_alpha_optional_without_skips(lib):
 
 def test_fwd_workspace_sizes(lib):
     ws = lib.sparse_attn_fwd_workspace_size
-    # pi-Attention with skip keys: (m, l) pairs plus a d-wide fp32 accumulator per row.
-    rows = 2 * 16 * 16384
-    assert ws(2, 16, 16, 16384, 64, BF16, PI, 256, 1024, 15, 0) == rows * 8 + rows * 64 * 4
+    # pi-Attention with skip keys: per row an (m, l) fp32 pair and a d-wide
+    # accumulator in the I/O dtype, for one chunk of (batch, head) slices: at
+    # most 128 MiB, split into balanced chunks.
+    rows = 32 * 16384                                   # 71.3 MB: one chunk
+    r256 = lambda x: -(-x // 256) * 256
+    assert ws(2, 16, 16, 16384, 64, BF16, PI, 256, 1024, 15, 0) == r256(rows * 8) + r256(rows * 64 * 2)
+    assert ws(1, 2, 2, 100, 64, F32, PI, 32, 64, 3, 0) == r256(2 * 100 * 8) + r256(2 * 100 * 64 * 4)
+    # 64 slices of 4.3 MB (fp32, d = 128, N = 8192) -> 3 chunks of 22 slices.
+    rows = 22 * 8192
+    assert ws(4, 16, 16, 8192, 128, F32, PI, 256, 1024, 15, 0) == r256(rows * 8) + r256(rows * 128 * 4)
     assert ws(1, 32, 32, 65536, 128, BF16, WINDOW, 1024, 0, 0, 0) == 0
     assert ws(4, 12, 12, 4096, 64, BF16, ECP, 0, 0, 0, 512) == 0
     assert ws(1, 2, 2, 256, 64, F32, PI, 32, 64, 0, 0) == 0          # M = 0

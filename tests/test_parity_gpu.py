@@ -234,6 +234,22 @@ def test_full_size_sampled(name):
     assert_close(o[rows], ref, "bf16", name)
 
 
+def test_pi_gqa_several_chunks_sampled():
+    """pi-Attention with GQA large enough that the skip pass and the prefill run
+    over several chunks of head groups (workspace reused between chunks)."""
+    w = Workload("pi_gqa_chunks", "pi", "bf16", 2, 32, 8, 32768, 64, k_win=200, pi=700, M=20,
+                 seed=71)
+    say("chunked %s" % (w,))
+    whole = w.B * w.Hq * w.N * (8 + 2 * w.d)          # skip state of every row at once
+    assert 0 < sa.fwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, torch.bfloat16, "pi", w.k_win,
+                                    w.pi, w.M) < whole / 2
+    q, k, v, a = prefill_inputs(w, device=DEV)
+    o = gpu_fwd(w, q, k, v, a).float().cpu().numpy().reshape(-1, w.d)
+    rows = _sample_rows(np.random.default_rng(7), w.B, w.Hq, w.N, 3000)
+    ref = oracle_fwd(w, q.cpu(), k.cpu(), v.cpu(), a.cpu(), rows=rows)
+    assert_close(o[rows], ref, "bf16", w.name)
+
+
 def test_full_size_window_loop_sampled():
     w = WORKLOADS["window_loop_bf16"]
     say("full-size %s" % w.name)
