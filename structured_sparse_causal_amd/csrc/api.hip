@@ -212,7 +212,7 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d
     return 0;
   int nw, chunk, hs, mm;
   decode_plan(Lmax, mode, k_win, pi, M, seg, &nw, &chunk, &hs, &mm);
-  return round_up((size_t)B * Hq * (nw + hs) * (d + 2) * sizeof(float), 256);
+  return round_up((size_t)B * Hq * (nw + hs) * (d + 4) * sizeof(float), 256);
 }
 
 int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,

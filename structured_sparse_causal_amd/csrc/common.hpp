@@ -27,6 +27,14 @@ typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load marked non-temporal: for data read exactly once (decode
+// cache rows), so it does not displace reusable lines from L2 and the
+// last-level cache.
+__device__ __forceinline__ u32x4 load_once16(const void *p) {
+  return __builtin_nontemporal_load((const u32x4 *)p);
+}
 
 // Running-max sentinel: finite, so exp2(sentinel - x) is 0 and sentinel - sentinel is 0.
 constexpr float kNegBig = -1.0e30f;

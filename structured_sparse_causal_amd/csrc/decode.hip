@@ -16,7 +16,10 @@
 // A operand, loaded straight from HBM in operand layout; queries of the group
 // are the columns), online softmax per head column, then O^T += V^T P^T on
 // v_mfma_f32_16x16x16bf16_1k with the V^T fragment read transposed from a
-// per-wave LDS slab (ds_read_b64_tr_b16).
+// per-wave LDS slab (ds_read_b64_tr_b16).  Each wave keeps one 16-row group
+// in flight while it consumes the previous one (kRing = 2 register buffers:
+// a deeper ring costs occupancy and measured slower); the four waves' partial
+// states are merged pairwise through LDS at the end.
 #include <type_traits>
 
 #include "common.hpp"
@@ -49,9 +52,9 @@ __device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
 
 // Rows of this split: count and position of row r.
 struct SplitRows {
-  int count, base, stride;  // position(r) = base - r*stride for skips, base + r otherwise
+  int count, base, step;  // position(r) = base + r*step: step 1 (window), -pi (skips)
   bool skip;
-  __device__ __forceinline__ int pos(int r) const { return skip ? base - r * stride : base + r; }
+  __device__ __forceinline__ int pos(int r) const { return base + r * step; }
 };
 
 __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int split) {
@@ -62,7 +65,7 @@ __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int spli
     const int e = min(a + p.chunk, i + 1);
     sr.count = e > a ? e - a : 0;
     sr.base = a;
-    sr.stride = 0;
+    sr.step = 1;
     sr.skip = false;
   } else {
     // Skip keys i - m*pi, m = m_min..M, that are >= 0 (all lie below lo).
@@ -71,22 +74,67 @@ __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int spli
     if (p.mode == kModePi && p.M >= p.m_min && first >= 0) cnt = min(p.M - p.m_min, first / p.pi) + 1;
     sr.count = cnt;
     sr.base = first;
-    sr.stride = p.pi;
+    sr.step = -p.pi;
     sr.skip = true;
   }
   return sr;
 }
 
 constexpr int kWaves = 4;
+constexpr int kRing = 2;   // 16-row groups per wave held in registers (kRing - 1 in flight)
+
+// One 16-row group of a wave in flight: K rows in MFMA A-operand layout
+// (lane (G, t) holds row t, dims 32*kk + 8*G .. +7) and the same rows of V as
+// 16-byte chunks (chunk lane + 64*u of the row-major 16 x D slab).  Cache rows
+// are read exactly once, with non-temporal loads: on this access pattern
+// (a 0.5 MB run per (sequence, KV head) at an 8 MB stride) they stream at
+// about 7 TB/s against about 5.8 TB/s for cached loads.
+template <int D>
+struct Group {
+  static constexpr int NK = D / 32, NV = D / 32;
+  bf16x8 k[NK];
+  u32x4 v[NV];
+};
+
+// Loads are unconditional (no per-lane branches, which would make the
+// compiler wait on each load right after issuing it): rows past the split's
+// end re-read its last row (scores masked, probabilities 0) and an empty split
+// reads `fallback`, an in-range row.
+template <int D>
+__device__ __forceinline__ Group<D> load_group(const bf16 *Kp, const bf16 *Vp, const SplitRows &sr, int r0,
+                                               int lane, int fallback) {
+  Group<D> g;
+  const int t = lane & 15, G = lane >> 4;
+  const int last = sr.count - 1;
+  const size_t krow = (size_t)(last >= 0 ? sr.pos(min(r0 + t, last)) : fallback) * D;
+#pragma unroll
+  for (int kk = 0; kk < Group<D>::NK; ++kk)
+    g.k[kk] = __builtin_bit_cast(bf16x8, load_once16(Kp + krow + 32 * kk + 8 * G));
+#pragma unroll
+  for (int u = 0; u < Group<D>::NV; ++u) {
+    const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+    const size_t vrow = (size_t)(last >= 0 ? sr.pos(min(r0 + row, last)) : fallback) * D;
+    g.v[u] = load_once16(Vp + vrow + col);
+  }
+  return g;
+}
+
+// Workspace entry of one (sequence, query head, split): max (log2 units), sum,
+// two pad words, then the d-wide unnormalised accumulator (16-byte aligned).
+template <int D>
+constexpr int ws_stride() { return D + 4; }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   constexpr bool kBF = sizeof(T) == 2;
   constexpr int LD = D + 8;
   constexpr int NDB = D / 16;
-  __shared__ __attribute__((aligned(16))) T Vs[kWaves][kBF ? 16 * LD : 1];
-  __shared__ float red_m[kWaves][16], red_l[kWaves][16];
-  __shared__ float red_acc[kWaves][16][D + 1];
+  // LDS: per-wave V slabs while streaming rows, then two slots for the
+  // cross-wave merge (accumulators in C layout, max and sum per lane).
+  constexpr int kSlabBytes = kBF ? kWaves * 16 * LD * 2 : 0;
+  constexpr int kSlotBytes = 64 * NDB * 16 + 2 * 64 * 4;
+  constexpr int kSmem = kSlabBytes > 2 * kSlotBytes ? kSlabBytes : 2 * kSlotBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = lane >> 4, t = lane & 15;
@@ -127,33 +175,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
   float m_run = kNegBig, l_run = 0.f;
-  T *vs = Vs[wave];
 
-  for (int r0 = 16 * wave; r0 < sr.count; r0 += 16 * kWaves) {
-    // ---- scores for rows r0 + 4G + jj (C layout), operand row r0 + t ---------
-    const bool rvalid = r0 + t < sr.count;
-    const int prow = sr.pos(min(r0 + t, sr.count - 1));
-    f32x4 s = f32x4{};
-#pragma unroll
-    for (int kk = 0; kk < NQF; ++kk) {
-      if constexpr (kBF) {
-        const bf16x8 a = rvalid ? *(const bf16x8 *)(Kp + (size_t)prow * D + 32 * kk + 8 * G) : bf16x8{};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], s, 0, 0, 0);
-      } else {
-        const float a = rvalid ? (float)Kp[(size_t)prow * D + 4 * kk + G] : 0.f;
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[kk], s, 0, 0, 0);
-      }
-    }
-    if constexpr (kBF) {
-      // Stage the 16 value rows for the transposed read.
-#pragma unroll
-      for (int ci = lane; ci < 16 * D / 8; ci += 64) {
-        const int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-        uint4 vv = make_uint4(0, 0, 0, 0);
-        if (r0 + row < sr.count) vv = *(const uint4 *)(Vp + (size_t)sr.pos(r0 + row) * D + col);
-        *(uint4 *)(vs + row * LD + col) = vv;
-      }
-    }
+  // Online softmax over the 4 score rows this lane holds (rows r0 + 4G + jj,
+  // head column t); returns them as probabilities.
+  auto softmax_step = [&](f32x4 s, int r0) -> f32x4 {
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -177,7 +202,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
       s[jj] = fast_exp2(fmaf(s[jj], p.scale_log2, nb));
       l_run += s[jj];
     }
-    if constexpr (kBF) {
+    return s;
+  };
+
+  if constexpr (kBF) {
+    // Rows are streamed in 16-row groups, wave w taking groups w, w+4, ...;
+    // a ring of kRing groups keeps kRing - 1 groups of loads in flight while
+    // one is consumed (memory latency is hidden by bytes in flight per wave).
+    bf16 *vs = (bf16 *)smem + wave * 16 * LD;
+    auto consume = [&](const Group<D> &cur, int r0) {
+      f32x4 s = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < NQF; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[kk], qf[kk], s, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < Group<D>::NV; ++u) {
+        const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+        *(u32x4 *)(vs + row * LD + col) = cur.v[u];
+      }
+      s = softmax_step(s, r0);
       bf16x4 pb;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) pb[jj] = (bf16)s[jj];
@@ -186,15 +228,36 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const T *src = vs + (4 * G + (t >> 2)) * LD + 16 * db + 4 * (t & 3);
+        const bf16 *src = vs + (4 * G + (t >> 2)) * LD + 16 * db + 4 * (t & 3);
         const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src);
-        const bf16x4 a = as_bf16x4(x);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(x), pb, acc[db], 0, 0, 0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else {
+    };
+    constexpr int kStep = 16 * kWaves;
+    Group<D> ring[kRing];
+#pragma unroll
+    for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, sr, 16 * wave + j * kStep, lane, i);
+    for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, sr, r0 + (j + kRing - 1) * kStep, lane, i);
+        if (r0 + j * kStep < sr.count) consume(ring[j], r0 + j * kStep);
+      }
+    }
+  } else {
+    for (int r0 = 16 * wave; r0 < sr.count; r0 += 16 * kWaves) {
+      const bool rvalid = r0 + t < sr.count;
+      const int prow = sr.pos(min(r0 + t, sr.count - 1));
+      f32x4 s = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < NQF; ++kk) {
+        const float a = rvalid ? (float)Kp[(size_t)prow * D + 4 * kk + G] : 0.f;
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[kk], s, 0, 0, 0);
+      }
+      s = softmax_step(s, r0);
       // k index of the 16x16x4 f32 product = lane group G <-> row r0 + 4G + jj.
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -210,67 +273,72 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     }
   }
 
-  // ---- merge the four waves, then write this split's partial state -------
+  // ---- merge the four waves pairwise through LDS (every lane keeps its C
+  // layout: head column t, dims 16*db + 4G + jj), then write the split ------
   l_run += wave_shfl_xor(l_run, 16);
   l_run += wave_shfl_xor(l_run, 32);
-  if (G == 0) {
-    red_m[wave][t] = m_run;
-    red_l[wave][t] = l_run;
-  }
+  auto publish = [&](int slot) {
+    f32x4 *A = (f32x4 *)(smem + slot * kSlotBytes);
+    float *ML = (float *)(A + NDB * 64);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) A[db * 64 + lane] = acc[db];
+    ML[lane] = m_run;
+    ML[64 + lane] = l_run;
+  };
+  auto absorb = [&](int slot) {
+    const f32x4 *A = (const f32x4 *)(smem + slot * kSlotBytes);
+    const float *ML = (const float *)(A + NDB * 64);
+    const float m1 = ML[lane], l1 = ML[64 + lane];
+    const float mn = fmaxf(m_run, m1);
+    const float f0 = fast_exp2(m_run - mn), f1 = fast_exp2(m1 - mn);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) red_acc[wave][t][16 * db + 4 * G + jj] = acc[db][jj];
+    for (int db = 0; db < NDB; ++db) acc[db] = acc[db] * f0 + A[db * 64 + lane] * f1;
+    l_run = l_run * f0 + l1 * f1;
+    m_run = mn;
+  };
+  __syncthreads();                    // the V slabs are free
+  if (wave >= 2) publish(wave - 2);
   __syncthreads();
-  // Thread (head hh, dims) merges: 256 threads = 16 heads x 16 dim lanes.
-  const int hh = threadIdx.x >> 4, dl = threadIdx.x & 15;
-  if (16 * hc + hh >= p.grp) return;
-  float mw[kWaves], mstar = kNegBig;
+  if (wave < 2) absorb(wave);
+  __syncthreads();
+  if (wave == 1) publish(0);
+  __syncthreads();
+  if (wave != 0) return;
+  absorb(0);
+  if (!hvalid) return;
+  float *wp = p.ws + (((size_t)b * p.Hq + hq) * p.nsplit + split) * ws_stride<D>();
+  if (G == 0) {
+    wp[0] = len_ok ? m_run : NAN;
+    wp[1] = l_run;
+  }
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    mw[w] = red_m[w][hh];
-    mstar = fmaxf(mstar, mw[w]);
-  }
-  float fw[kWaves], lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    fw[w] = fast_exp2(mw[w] - mstar);
-    lsum += red_l[w][hh] * fw[w];
-  }
-  const int hq_out = g * p.grp + 16 * hc + hh;
-  float *wp = p.ws + (((size_t)b * p.Hq + hq_out) * p.nsplit + split) * (D + 2);
-  if (!len_ok) mstar = NAN;
-  if (dl == 0) {
-    wp[0] = mstar;
-    wp[1] = lsum;
-  }
-  for (int dim = dl; dim < D; dim += 16) {
-    float a = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) a += red_acc[w][hh][dim] * fw[w];
-    wp[2 + dim] = a;
-  }
+  for (int db = 0; db < NDB; ++db) *(f32x4 *)(wp + 4 + 16 * db + 4 * G) = acc[db];
 }
 
-// Merge the split partials of one (sequence, query head) and normalise.
+// Merge the split partials of one (sequence, query head) and normalise: one
+// thread per output dimension, an online log-sum-exp merge over the splits.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(Params p) {
+__global__ __launch_bounds__(D) void decode_combine_kernel(Params p) {
   const int row = blockIdx.x;  // b*Hq + hq
-  const float *wp = p.ws + (size_t)row * p.nsplit * (D + 2);
-  float mstar = kNegBig;
-  for (int s = 0; s < p.nsplit; ++s) mstar = fmaxf(mstar, wp[s * (D + 2)]);
+  const int dim = threadIdx.x;
+  const float *wp = p.ws + (size_t)row * p.nsplit * ws_stride<D>();
+  float m = kNegBig, l = 0.f, a = 0.f;
   bool bad = false;
-  for (int s = 0; s < p.nsplit; ++s) bad |= (wp[s * (D + 2)] != wp[s * (D + 2)]);
-  float l = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) l += wp[s * (D + 2) + 1] * fast_exp2(wp[s * (D + 2)] - mstar);
-  for (int dim = threadIdx.x; dim < D; dim += blockDim.x) {
-    float a = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) a += wp[s * (D + 2) + 2 + dim] * fast_exp2(wp[s * (D + 2)] - mstar);
-    const float o = bad ? NAN : a / l;
-    T *op = (T *)p.o + (size_t)row * D + dim;
-    if constexpr (sizeof(T) == 2) *(unsigned short *)op = f32_to_bf16_bits(o);
-    else *op = o;
+#pragma unroll 4
+  for (int s = 0; s < p.nsplit; ++s) {
+    const float *e = wp + s * ws_stride<D>();
+    const float ms = e[0], ls = e[1], as = e[4 + dim];
+    bad |= ms != ms;
+    const float mn = fmaxf(m, ms);
+    const float f0 = fast_exp2(m - mn), f1 = fast_exp2(ms - mn);
+    l = l * f0 + ls * f1;
+    a = a * f0 + as * f1;
+    m = mn;
   }
+  const float o = bad ? NAN : a / l;
+  T *op = (T *)p.o + (size_t)row * D + dim;
+  if constexpr (sizeof(T) == 2) *(unsigned short *)op = f32_to_bf16_bits(o);
+  else *op = o;
 }
 
 template <typename T, int D>
@@ -286,7 +354,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(p.nsplit, a.Hkv * p.hchunks, a.B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(128), 0, s, p);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(D), 0, s, p);
   return hipGetLastError();
 }
 

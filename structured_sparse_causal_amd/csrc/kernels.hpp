@@ -39,7 +39,7 @@ struct DecodeArgs {
   const int *lens;
   const float *alpha;   // [B,Hq] or nullptr
   void *o;
-  float *ws;            // [B*Hq][nsplit][d+2]
+  float *ws;            // [B*Hq][nsplit][d+4]: max, sum, 2 pad, accumulator
   int B, Hq, Hkv, Lmax, d, dtype;
   int mode, k_win, pi, M, seg, m_min;
   int n_wsplit, chunk, has_skip, nsplit;

@@ -121,9 +121,9 @@ def test_decode_rejects(lib, kw, code):
 def test_decode_workspace_size(lib):
     ws = lib.sparse_attn_decode_workspace_size
     # 2049 window rows -> 9 splits of 256, plus one split for the skip keys.
-    assert ws(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0) == 64 * 32 * 10 * 130 * 4
-    assert ws(64, 32, 8, 32768, 128, BF16, WINDOW, 2048, 0, 0, 0) == 64 * 32 * 9 * 130 * 4
-    assert ws(1, 1, 1, 100, 64, F32, ECP, 0, 0, 0, 512) == 256 * ((1 * 1 * 1 * 66 * 4 + 255) // 256)
+    assert ws(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0) == 64 * 32 * 10 * 132 * 4
+    assert ws(64, 32, 8, 32768, 128, BF16, WINDOW, 2048, 0, 0, 0) == 64 * 32 * 9 * 132 * 4
+    assert ws(1, 1, 1, 100, 64, F32, ECP, 0, 0, 0, 512) == 256 * ((1 * 1 * 1 * 68 * 4 + 255) // 256)
     assert ws(1, 1, 1, 100, 60, F32, ECP, 0, 0, 0, 512) == 0
 
 
