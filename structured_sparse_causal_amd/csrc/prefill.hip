@@ -13,10 +13,10 @@
 // O^T = V^T P^T; the V^T fragment comes straight from the row-major V tile
 // through ds_read_b64_tr_b16.
 //
-// Pipelining: K/V tiles are double-buffered in LDS.  While a wave computes on
-// tile t, the workgroup's global loads of tile t+1 are already in flight into
-// registers; they are written to the other LDS buffer after the compute, so
-// one barrier per tile suffices and HBM latency hides behind the MFMA work.
+// Pipelining (bf16): K/V tiles are double-buffered in LDS and loaded straight
+// from HBM into LDS; while the waves compute on tile t, the direct-to-LDS
+// loads of tile t+1 are in flight, and one barrier per tile hands the buffers
+// over.  Without staging registers the d = 64 kernel fits 4 waves per SIMD.
 //
 // The softmax is online in log2 units with lazy rescaling (the running max
 // only moves when a tile raises it by more than 8, so exp2 arguments stay
@@ -55,23 +55,6 @@ __device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
   return lo > 0 ? lo : 0;
 }
 
-// LDS tile geometry.  K rows are read as 16-byte MFMA fragments by 32 lanes at
-// once (one row each): a 16-byte row pad spreads them over all banks.  V rows
-// are read by ds_read_b64_tr_b16 (4 rows x 32 bytes per 16 lanes, two such
-// groups 32 bytes apart per half-wave): a row stride of 64 bytes modulo 256
-// keeps both groups on disjoint banks.  fp32 tiles use plain 4-byte reads.
-template <typename T, int D>
-struct Tile {
-  static constexpr bool kBF = sizeof(T) == 2;
-  static constexpr int LDK = D + (kBF ? 8 : 4);                   // elements
-  static constexpr int LDV = kBF ? (D == 64 ? 96 : 160) : D + 4;  // elements
-  static constexpr int VEC = 16 / sizeof(T);                       // elements per 16 bytes
-  static constexpr int CPR = D / VEC;                              // 16-byte chunks per row
-  static constexpr int PER_THREAD = BN * CPR / 256;                // chunks per thread per tensor
-  static constexpr int NBUF = kBF ? 2 : 1;
-  static constexpr int KSZ = BN * LDK, VSZ = BN * LDV;
-};
-
 __device__ __forceinline__ float half_swap_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -82,13 +65,190 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
-  using TL = Tile<T, D>;
-  constexpr bool kBF = TL::kBF;
-  constexpr int LDK = TL::LDK, LDV = TL::LDV;
-  __shared__ __attribute__((aligned(16))) T Ks[TL::NBUF][TL::KSZ];
-  __shared__ __attribute__((aligned(16))) T Vs[TL::NBUF][TL::VSZ];
+// fp32 I/O (small problems, exact-arithmetic checks): the same walk over key
+// tiles with v_mfma_f32_32x32x2f32, one LDS buffer (rows padded by 16 bytes)
+// and plain 4-byte operand reads.
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
+  constexpr int LD = D + 4;                 // floats per LDS row
+  constexpr int CPR = D / 4;                // 16-byte chunks per row
+  constexpr int PER_THREAD = BN * CPR / 256;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) float Ks[BN * LD];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * LD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
+  const int logical = xcd_remap(blockIdx.x, p.total);
+  const int qb = p.nqb - 1 - logical % p.nqb, bh = logical / p.nqb;
+  const int hq = bh % p.Hq, b = bh / p.Hq;
+  const int g = hq / (p.Hq / p.Hkv);
+  const int N = p.N;
+  const int i0 = qb * BM, q0 = i0 + wave * 32, qi = q0 + c;
+  const bool qvalid = qi < N;
+
+  const float *Qp = (const float *)p.q + (size_t)bh * N * D;
+  const float *Kp = (const float *)p.k + (size_t)(b * p.Hkv + g) * N * D;
+  const float *Vp = (const float *)p.v + (size_t)(b * p.Hkv + g) * N * D;
+
+  const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
+  float bias = 0.f;  // log2 of the local prior
+  if (p.mode == kModePi && p.alpha != nullptr && qvalid) bias = __log2f(p.alpha[(size_t)bh * N + qi]);
+
+  float qf[D / 2];
+#pragma unroll
+  for (int kk = 0; kk < D / 2; ++kk) qf[kk] = qvalid ? Qp[(size_t)qi * D + 2 * kk + h] : 0.f;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  float m_run = kNegBig, l_run = 0.f;
+
+  // Seed with the skip-key partial state (pi-Attention union, one softmax).
+  if (p.skip_ml != nullptr && qvalid && qi >= p.skip_first) {
+    const size_t row = (size_t)bh * N + qi;
+    m_run = p.skip_ml[2 * row];
+    if (h == 0) l_run = p.skip_ml[2 * row + 1];
+    const float *ap = (const float *)p.skip_acc + row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 x = *(const f32x4 *)(ap + 32 * db + 8 * j4 + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * j4 + e] = x[e];
+      }
+  }
+
+  const int hi_wg = min(i0 + BM - 1, N - 1);
+  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
+  const int ntiles = (hi_wg - t_begin) / BN + 1;
+  const bool wave_live = q0 < N;
+  const int w_hi = min(q0 + 31, N - 1);
+  const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
+  const float sl2 = p.scale_log2;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t_begin + t * BN;
+    __syncthreads();   // everyone is done with the previous tile
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + 256 * r;
+      const int row = ci / CPR, col = (ci % CPR) * 4;
+      const int key = min(j0 + row, N - 1);   // rows past N: masked / probability 0
+      *(float4 *)&Ks[row * LD + col] = *(const float4 *)(Kp + (size_t)key * D + col);
+      *(float4 *)&Vs[row * LD + col] = *(const float4 *)(Vp + (size_t)key * D + col);
+    }
+    __syncthreads();
+    if (!(wave_live && j0 <= w_hi && j0 + BN - 1 >= w_lo)) continue;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const float *krow = Ks + (32 * kb + c) * LD;
+#pragma unroll
+      for (int kk = 0; kk < D / 2; ++kk) s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk + h], qf[kk], s[kb], 0, 0, 0);
+    }
+    // mask: key j visible to query i iff lo(i) <= j <= i (tile-local index of
+    // register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4)
+    const int a0 = lo_i - j0 - 4 * h, span = qi - lo_i;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int off = 32 * kb + 8 * (jj >> 2) + (jj & 3);
+        if ((unsigned)(off - a0) > (unsigned)span) s[kb][jj] = -INFINITY;
+      }
+    float mx = s[0][0];
+#pragma unroll
+    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s[0][jj]);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[1][jj]);
+    mx = half_swap_max(mx);
+    const float m_new = mx * sl2 + bias;
+    if (__any(m_new > m_run + kTau)) {
+      const float mr = fmaxf(m_run, m_new);
+      const float f = fast_exp2(m_run - mr);
+      l_run *= f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= f;
+      m_run = mr;
+    }
+    const float nb = bias - m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        s[kb][jj] = fast_exp2(fmaf(s[kb][jj], sl2, nb));
+        l_run += s[kb][jj];
+      }
+    // O^T += V^T P^T: k index of the 32x32x2 product = lane half h <-> key
+    // 32kb + 8(tt/4) + 4h + tt%4.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        const float *vrow = Vs + (32 * kb + 8 * (tt >> 2) + 4 * h + (tt & 3)) * LD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * db + c], s[kb][tt], acc[db], 0, 0, 0);
+      }
+  }
+
+  const float l_tot = half_swap_sum(l_run);
+  if (!qvalid) return;
+  const float inv = 1.0f / l_tot;
+  float *op = (float *)p.o + ((size_t)bh * N + qi) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
+      *(f32x4 *)(op + 32 * db + 8 * j4 + 4 * h) = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 I/O.  K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4:
+// no staging registers), rows unpadded with the 16-byte chunks of row r
+// permuted by chunk ^ swz(r).  swz makes both LDS read patterns conflict-free:
+//  * K fragment reads (16 lanes = 16 consecutive rows, one chunk each) need
+//    swz to be a bijection on rows of equal bank offset;
+//  * transposed V reads (32 lanes = 4 consecutive rows x 4 chunks) need the
+//    4 rows' 4-chunk groups to land on disjoint banks.
+// d = 64 (128-byte rows, two rows per bank sweep): swz(r) = (r1 << 2) | r3r2;
+// d = 128 (256-byte rows): swz(r) = (r1r0 << 2) | r3r2.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// One 16-byte direct-to-LDS load per lane: lane L's bytes land at
+// lds_base + 16 * L.  Issued through inline asm so that the compiler does not
+// wait for it before unrelated LDS reads; the caller waits (vmcnt) itself.
+__device__ __forceinline__ void dma16(const void *gbase, unsigned voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
+  constexpr int RB = D * 2;              // bytes per K/V row
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int TILE = BN * RB;          // bytes per K or V tile
+  constexpr int PER_WAVE = TILE / 1024 / 4;  // DMA instructions per wave per tile
+  constexpr int NQF = D / 16;            // k-steps of the 32x32x16 score product
+  constexpr int NDB = D / 32;            // 32-dim blocks of O^T
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
@@ -102,29 +262,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
   const int i0 = qb * BM, q0 = i0 + wave * 32, qi = q0 + c;
   const bool qvalid = qi < N;
 
-  const T *Qp = (const T *)p.q + (size_t)bh * N * D;
-  const T *Kp = (const T *)p.k + (size_t)(b * p.Hkv + g) * N * D;
-  const T *Vp = (const T *)p.v + (size_t)(b * p.Hkv + g) * N * D;
+  const bf16 *Qp = (const bf16 *)p.q + (size_t)bh * N * D;
+  const bf16 *Kp = (const bf16 *)p.k + (size_t)(b * p.Hkv + g) * N * D;
+  const bf16 *Vp = (const bf16 *)p.v + (size_t)(b * p.Hkv + g) * N * D;
 
-  // ---- per-lane query state --------------------------------------------
   const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
   float bias = 0.f;  // log2 of the local prior
   if (p.mode == kModePi && p.alpha != nullptr && qvalid) bias = __log2f(p.alpha[(size_t)bh * N + qi]);
 
-  constexpr int NQF = kBF ? D / 16 : D / 2;
-  typedef typename std::conditional<kBF, bf16x8, float>::type QFrag;
-  QFrag qf[NQF];
+  bf16x8 qf[NQF];
 #pragma unroll
-  for (int kk = 0; kk < NQF; ++kk) {
-    if constexpr (kBF) {
-      if (qvalid) qf[kk] = *(const bf16x8 *)(Qp + (size_t)qi * D + 16 * kk + 8 * h);
-      else qf[kk] = bf16x8{};
-    } else {
-      qf[kk] = qvalid ? (float)Qp[(size_t)qi * D + 2 * kk + h] : 0.f;
-    }
-  }
+  for (int kk = 0; kk < NQF; ++kk)
+    qf[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)qi * D + 16 * kk + 8 * h) : bf16x8{};
 
-  constexpr int NDB = D / 32;
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -135,23 +285,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
     const size_t row = (size_t)bh * N + qi;
     m_run = p.skip_ml[2 * row];
     if (h == 0) l_run = p.skip_ml[2 * row + 1];
-    const T *ap = (const T *)p.skip_acc + row * D;
+    const bf16 *ap = (const bf16 *)p.skip_acc + row * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        const T *src = ap + 32 * db + 8 * j4 + 4 * h;
-        if constexpr (kBF) {
-          const ushort4 u = *(const ushort4 *)src;
-          acc[db][4 * j4 + 0] = bf16_to_f32(u.x);
-          acc[db][4 * j4 + 1] = bf16_to_f32(u.y);
-          acc[db][4 * j4 + 2] = bf16_to_f32(u.z);
-          acc[db][4 * j4 + 3] = bf16_to_f32(u.w);
-        } else {
-          const f32x4 x = *(const f32x4 *)src;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[db][4 * j4 + e] = x[e];
-        }
+        const ushort4 u = *(const ushort4 *)(ap + 32 * db + 8 * j4 + 4 * h);
+        acc[db][4 * j4 + 0] = bf16_to_f32(u.x);
+        acc[db][4 * j4 + 1] = bf16_to_f32(u.y);
+        acc[db][4 * j4 + 2] = bf16_to_f32(u.z);
+        acc[db][4 * j4 + 3] = bf16_to_f32(u.w);
       }
   }
 
@@ -166,61 +309,73 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
   const bool w_allvalid = q0 + 31 < N;
   const float sl2 = p.scale_log2;
 
-  // ---- cooperative staging: global -> registers -> LDS --------------------
-  uint4 kreg[TL::PER_THREAD], vreg[TL::PER_THREAD];
-  auto load_tile = [&](int j0) {
+  // ---- direct-to-LDS staging of one K and one V tile -----------------------
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  auto stage = [&](int j0, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < TL::PER_THREAD; ++r) {
-      const int ci = tid + 256 * r;
-      const int row = ci / TL::CPR, col = (ci % TL::CPR) * TL::VEC;
-      const int key = j0 + row;
-      if (key < N) {
-        kreg[r] = *(const uint4 *)(Kp + (size_t)key * D + col);
-        vreg[r] = *(const uint4 *)(Vp + (size_t)key * D + col);
-      } else {
-        kreg[r] = make_uint4(0, 0, 0, 0);
-        vreg[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < TL::PER_THREAD; ++r) {
-      const int ci = tid + 256 * r;
-      const int row = ci / TL::CPR, col = (ci % TL::CPR) * TL::VEC;
-      *(uint4 *)(&Ks[buf][row * LDK + col]) = kreg[r];
-      *(uint4 *)(&Vs[buf][row * LDV + col]) = vreg[r];
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int slot = PER_WAVE * wave + u;             // 1 KB slot of the tile
+      const int pch = 64 * slot + lane;                 // chunk position in LDS
+      const int row = pch / CPR;
+      const int src = (pch % CPR) ^ tile_swz<D>(row);   // chunk held there
+      const int key = min(j0 + row, N - 1);             // rows past N: masked / probability 0
+      const unsigned voff = (unsigned)((key * D + src * 8) * 2);
+      const unsigned kdst = __builtin_amdgcn_readfirstlane(lds0 + buf * TILE + 1024 * slot);
+      dma16(Kp, voff, kdst);
+      dma16(Vp, voff, kdst + 2 * TILE);
     }
   };
 
-  load_tile(t_begin);
-  store_tile(0);
+  // Per-lane LDS byte offsets inside a tile (buffer and key-block offsets are
+  // added as constants).  K: row c of a 32-row block, chunk 2kk+h.
+  int koff[NQF];
+  {
+    const int sw = tile_swz<D>(c);
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk) koff[kk] = c * RB + (((2 * kk + h) ^ sw) << 4);
+  }
+  // V^T fragments: rows 16kk + 4h + tt/4 (+8), bytes 64db + 32(G&1) + 8(tt&3).
+  const int G = lane >> 4, tt = lane & 15;
+  int voffs[NDB][2];
+  {
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      const int r = 4 * h + (tt >> 2) + 8 * sidx;
+      const int sw = tile_swz<D>(r);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int byte = 64 * db + 32 * (G & 1) + 8 * (tt & 3);
+        voffs[db][sidx] = r * RB + ((((byte >> 4) ^ sw)) << 4) + (byte & 15);
+      }
+    }
+  }
+
+  // Settle every compiler-visible load (q, alpha, skip state) here, so no
+  // wait for them is placed inside the loop, where it would also stall on the
+  // in-flight tile.
+  __builtin_amdgcn_s_waitcnt(0);
+  stage(t_begin, 0);
+  wait_dma();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t_begin + t * BN;
-    const int buf = TL::NBUF == 2 ? (t & 1) : 0;
+    const int buf = t & 1;
     const bool more = t + 1 < ntiles;
-    if (TL::NBUF == 2 && more) load_tile(j0 + BN);   // in flight during the compute below
+    if (more) stage(j0 + BN, buf ^ 1);   // lands during the compute below
 
     if (wave_live && j0 <= w_hi && j0 + BN - 1 >= w_lo) {
-      const T *KB = Ks[buf];
-      const T *VB = Vs[buf];
+      const char *KB = smem + buf * TILE;
+      const char *VB = smem + (2 + buf) * TILE;
       // ---- S^T = K Q^T for the 64-key tile: two 32x32 blocks -------------------
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const T *krow = KB + (32 * kb + c) * LDK;
 #pragma unroll
         for (int kk = 0; kk < NQF; ++kk) {
-          if constexpr (kBF) {
-            const bf16x8 a = *(const bf16x8 *)(krow + 16 * kk + 8 * h);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-          } else {
-            const float a = krow[2 * kk + h];
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], s[kb], 0, 0, 0);
-          }
+          const bf16x8 a = *(const bf16x8 *)(KB + 32 * kb * RB + koff[kk]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
         }
       }
 
@@ -267,45 +422,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
       l_run += lsum;
 
       // ---- O^T += V^T P^T ------------------------------------------------------
-      if constexpr (kBF) {
-        const int G = lane >> 4, tt = lane & 15;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          bf16x8 pb;
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 pb;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[kk >> 1][8 * (kk & 1) + e];
+        for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[kk >> 1][8 * (kk & 1) + e];
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int col = 32 * db + 16 * (G & 1) + 4 * (tt & 3);
-            const T *r0 = VB + (16 * kk + 4 * h + (tt >> 2)) * LDV + col;
-            const T *r1 = r0 + 8 * LDV;
-            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)r0);
-            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)r1);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(lo, hi), pb, acc[db], 0, 0, 0);
-          }
+        for (int db = 0; db < NDB; ++db) {
+          const char *base = VB + 16 * kk * RB;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(base + voffs[db][0]));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(base + voffs[db][1]));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(lo, hi), pb, acc[db], 0, 0, 0);
         }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int tt = 0; tt < 16; ++tt) {
-            const T *vrow = VB + (32 * kb + 8 * (tt >> 2) + 4 * h + (tt & 3)) * LDV;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * db + c], s[kb][tt], acc[db], 0, 0, 0);
-          }
       }
     }
 
-    if (more) {
-      if (TL::NBUF == 2) {
-        store_tile(buf ^ 1);
-      } else {
-        __syncthreads();          // single buffer: everyone is done reading it
-        load_tile(j0 + BN);
-        store_tile(0);
-      }
-    }
+    if (more) wait_dma();
     __syncthreads();
   }
 
@@ -313,25 +445,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
   const float l_tot = half_swap_sum(l_run);
   if (!qvalid) return;
   const float inv = 1.0f / l_tot;
-  T *op = (T *)p.o + ((size_t)bh * N + qi) * D;
+  bf16 *op = (bf16 *)p.o + ((size_t)bh * N + qi) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-      const int dim = 32 * db + 8 * j4 + 4 * h;
-      if constexpr (kBF) {
-        ushort4 u;
-        u.x = f32_to_bf16_bits(acc[db][4 * j4 + 0] * inv);
-        u.y = f32_to_bf16_bits(acc[db][4 * j4 + 1] * inv);
-        u.z = f32_to_bf16_bits(acc[db][4 * j4 + 2] * inv);
-        u.w = f32_to_bf16_bits(acc[db][4 * j4 + 3] * inv);
-        *(ushort4 *)(op + dim) = u;
-      } else {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
-        *(f32x4 *)(op + dim) = x;
-      }
+      ushort4 u;
+      u.x = f32_to_bf16_bits(acc[db][4 * j4 + 0] * inv);
+      u.y = f32_to_bf16_bits(acc[db][4 * j4 + 1] * inv);
+      u.z = f32_to_bf16_bits(acc[db][4 * j4 + 2] * inv);
+      u.w = f32_to_bf16_bits(acc[db][4 * j4 + 3] * inv);
+      *(ushort4 *)(op + 32 * db + 8 * j4 + 4 * h) = u;
     }
 }
 
@@ -345,7 +469,8 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   p.total = a.B * a.Hq * p.nqb;
   p.skip_first = a.skip_first;
   p.scale_log2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((prefill_kernel<T, D>), dim3(p.total), dim3(256), 0, s, p);
+  if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
