@@ -43,6 +43,8 @@ struct Params {
   const float *skip_ml;
   const void *skip_acc;
   int N, Hq, Hkv, mode, k_win, seg, nqb, total, skip_first;
+  int heads_per_xcd;   // > 0: heavy-first block order per XCD (see block_of)
+  int ecp_J, ecp_C;    // ECP blocks per half-segment and half-segments (0: none)
   float scale_log2;
 };
 
@@ -53,6 +55,50 @@ __device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
   }
   const int lo = i - k_win;
   return lo > 0 ? lo : 0;
+}
+
+// Work order.  A query block's cost is its number of key tiles, which varies
+// with the block: ECP blocks in half-segment 0 and early in a half-segment are
+// light, causal window blocks near position 0 are light.  Blocks are handed
+// out heaviest first, so the light ones fill the grid's tail (list scheduling
+// by decreasing cost).  The grid is split into 8 contiguous ranges, one per
+// XCD (xcd_remap); each XCD owns heads_per_xcd whole heads (their K/V stay
+// in its L2) and walks them in cost rank order: all heads' heaviest blocks,
+// then the next, and so on.  Otherwise (heads not a multiple of 8, or block
+// costs nearly equal) each head's blocks run last-to-first.
+struct BlockId {
+  int bh, qb;
+};
+
+__device__ __forceinline__ BlockId block_of(const Params &p, int bid) {
+  const int logical = xcd_remap(bid, p.total);
+  BlockId r;
+  if (p.heads_per_xcd <= 0) {
+    r.qb = p.nqb - 1 - logical % p.nqb;
+    r.bh = logical / p.nqb;
+    return r;
+  }
+  const int per = p.total / 8;
+  const int x = logical / per, idx = logical - x * per;
+  const int rank = idx / p.heads_per_xcd;
+  r.bh = x * p.heads_per_xcd + (idx - rank * p.heads_per_xcd);
+  if (p.ecp_J > 0) {
+    // ECP with whole half-segments: cost depends on the block's position j in
+    // its half-segment (heavier later) and on c > 0.
+    const int J = p.ecp_J, C = p.ecp_C;
+    int j, c;
+    if (rank < J * (C - 1)) {
+      j = J - 1 - rank / (C - 1);
+      c = 1 + rank % (C - 1);
+    } else {
+      j = J - 1 - (rank - J * (C - 1));
+      c = 0;
+    }
+    r.qb = c * J + j;
+  } else {
+    r.qb = p.nqb - 1 - rank;
+  }
+  return r;
 }
 
 __device__ __forceinline__ float half_swap_max(float x) {
@@ -79,8 +125,8 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, p.total);
-  const int qb = p.nqb - 1 - logical % p.nqb, bh = logical / p.nqb;
+  const BlockId blk = block_of(p, blockIdx.x);
+  const int qb = blk.qb, bh = blk.bh;
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int g = hq / (p.Hq / p.Hkv);
   const int N = p.N;
@@ -252,10 +298,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, p.total);
-  // Within a head the blocks run last-to-first: late blocks have the longest
-  // key ranges (ECP, causal edges), so the light ones form the grid's tail.
-  const int qb = p.nqb - 1 - logical % p.nqb, bh = logical / p.nqb;
+  const BlockId blk = block_of(p, blockIdx.x);
+  const int qb = blk.qb, bh = blk.bh;
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int g = hq / (p.Hq / p.Hkv);
   const int N = p.N;
@@ -468,6 +512,16 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   p.nqb = (a.N + BM - 1) / BM;
   p.total = a.B * a.Hq * p.nqb;
   p.skip_first = a.skip_first;
+  // Rank order pays where block costs vary a lot (ECP, near-dense causal
+  // windows); narrow windows cost the same per block and keep head order.
+  const int BH = a.B * a.Hq;
+  const bool uneven = a.mode == kModeEcp || (long long)a.k_win * 4 >= a.N;
+  p.heads_per_xcd = (uneven && BH % 8 == 0) ? BH / 8 : 0;
+  p.ecp_J = p.ecp_C = 0;
+  if (a.mode == kModeEcp && a.seg % BM == 0 && a.N % a.seg == 0) {
+    p.ecp_J = a.seg / BM;
+    p.ecp_C = a.N / a.seg;
+  }
   p.scale_log2 = kLog2e / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
   else hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
