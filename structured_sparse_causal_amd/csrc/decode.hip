@@ -83,17 +83,16 @@ __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int spli
 constexpr int kWaves = 4;
 constexpr int kRing = 2;   // 16-row groups per wave held in registers (kRing - 1 in flight)
 
-// One 16-row group of a wave in flight: K rows in MFMA A-operand layout
-// (lane (G, t) holds row t, dims 32*kk + 8*G .. +7) and the same rows of V as
-// 16-byte chunks (chunk lane + 64*u of the row-major 16 x D slab).  Cache rows
-// are read exactly once, with non-temporal loads: on this access pattern
-// (a 0.5 MB run per (sequence, KV head) at an 8 MB stride) they stream at
-// about 7 TB/s against about 5.8 TB/s for cached loads.
+// One 16-row group of a wave in flight: the 16 rows of K and of V as 16-byte
+// chunks (chunk lane + 64*u of the row-major 16 x D block, so every load
+// instruction reads whole 128-byte lines).  Cache rows are read exactly once,
+// with non-temporal loads: on this access pattern (a 0.5 MB run per
+// (sequence, KV head) at an 8 MB stride) they stream at about 7 TB/s against
+// about 5.8 TB/s for cached loads.
 template <int D>
 struct Group {
-  static constexpr int NK = D / 32, NV = D / 32;
-  bf16x8 k[NK];
-  u32x4 v[NV];
+  static constexpr int NC = D / 32;   // chunks per lane per tensor
+  u32x4 k[NC], v[NC];
 };
 
 // Loads are unconditional (no per-lane branches, which would make the
@@ -104,17 +103,13 @@ template <int D>
 __device__ __forceinline__ Group<D> load_group(const bf16 *Kp, const bf16 *Vp, const SplitRows &sr, int r0,
                                                int lane, int fallback) {
   Group<D> g;
-  const int t = lane & 15, G = lane >> 4;
   const int last = sr.count - 1;
-  const size_t krow = (size_t)(last >= 0 ? sr.pos(min(r0 + t, last)) : fallback) * D;
 #pragma unroll
-  for (int kk = 0; kk < Group<D>::NK; ++kk)
-    g.k[kk] = __builtin_bit_cast(bf16x8, load_once16(Kp + krow + 32 * kk + 8 * G));
-#pragma unroll
-  for (int u = 0; u < Group<D>::NV; ++u) {
+  for (int u = 0; u < Group<D>::NC; ++u) {
     const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-    const size_t vrow = (size_t)(last >= 0 ? sr.pos(min(r0 + row, last)) : fallback) * D;
-    g.v[u] = load_once16(Vp + vrow + col);
+    const size_t off = (size_t)(last >= 0 ? sr.pos(min(r0 + row, last)) : fallback) * D + col;
+    g.k[u] = load_once16(Kp + off);
+    g.v[u] = load_once16(Vp + off);
   }
   return g;
 }
@@ -315,6 +310,232 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   for (int db = 0; db < NDB; ++db) *(f32x4 *)(wp + 4 + 16 * db + 4 * G) = acc[db];
 }
 
+// ---------------------------------------------------------------------------
+// bf16 decode.  Scores as in the fp32 kernel (S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16, query heads of the group as columns), but O is
+// accumulated with v_mfma_f32_4x4x4bf16_1k, whose 16 independent 4x4 blocks
+// fit a GQA group of 4 query heads exactly:
+//   block b (lanes 4b..4b+3):  O_b[head i][dim 4b+j] += P[head i][row k] V[row k][dim 4b+j]
+//   A: lane 4b+i holds P[head i][rows 4q..4q+3] (the same for every block),
+//   B: lane 4b+j holds V[rows 4q..4q+3][dim 4b+j] (a transposed LDS read),
+//   C: lane 4b+j, register i holds O[head i][dim 4b+j].
+// One instruction covers 64 dims of 4 heads, so the accumulator is 4 registers
+// per 64 dims and 4 heads (instead of 16 per 64 dims with 16 head columns), and
+// more waves fit per SIMD.  HC4 = 4-head chunks per workgroup (heads of the
+// group handled by one workgroup, up to 16).
+// ---------------------------------------------------------------------------
+template <int D, int HC4>
+__global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
+  // Per-wave slabs of the group's 16 rows.  K: row stride 16 bytes mod 256,
+  // so the 16 rows of an A-fragment read hit distinct banks.  V: row stride
+  // 64 bytes mod 256, so the 4 rows x 2 column groups of a 32-lane transposed
+  // read cover all 64 banks once.
+  constexpr int LDK = D + 8;
+  constexpr int LD = D == 64 ? 96 : 160;
+  constexpr int NH = D / 64;          // 64-dim halves of O
+  constexpr int NQF = D / 32;
+  constexpr int NHD = 4 * HC4;        // heads per workgroup
+  constexpr int kWaveSlab = 16 * (LDK + LD) * 2;
+  constexpr int kSlabBytes = kWaves * kWaveSlab;
+  constexpr int kSlotBytes = HC4 * NH * 64 * 16 + 2 * NHD * 4;
+  constexpr int kSmem = kSlabBytes > 2 * kSlotBytes ? kSlabBytes : 2 * kSlotBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = lane >> 4, t = lane & 15;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
+  const int b = blockIdx.z;
+  const int len = p.lens[b];
+  const bool len_ok = len >= 1 && len <= p.Lmax;
+  const int i = len_ok ? len - 1 : 0;
+  const int head = 16 * hc + t;               // score column t = head of the group
+  const bool hvalid = head < p.grp && t < NHD;
+  const int hq = g * p.grp + head;
+  const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lmax * D;
+  const bf16 *Kp = (const bf16 *)p.kc + kvoff;
+  const bf16 *Vp = (const bf16 *)p.vc + kvoff;
+  const bf16 *Qp = (const bf16 *)p.q + ((size_t)b * p.Hq + hq) * D;
+
+  SplitRows sr = split_rows(p, i, split);
+  if (!len_ok) sr.count = 0;
+
+  float bias = 0.f;
+  if (p.mode == kModePi && p.alpha != nullptr && hvalid) {
+    const float a = p.alpha[(size_t)b * p.Hq + hq];
+    bias = sr.skip ? __log2f(1.0f - a) : __log2f(a);
+  }
+
+  bf16x8 qf[NQF];
+#pragma unroll
+  for (int kk = 0; kk < NQF; ++kk) qf[kk] = hvalid ? *(const bf16x8 *)(Qp + 32 * kk + 8 * G) : bf16x8{};
+
+  f32x4 acc[HC4][NH];
+#pragma unroll
+  for (int c4 = 0; c4 < HC4; ++c4)
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) acc[c4][hh] = f32x4{};
+  float m_run = kNegBig, l_run = 0.f;   // score layout: head t
+
+  bf16 *ks = (bf16 *)(smem + wave * kWaveSlab);
+  bf16 *vs = ks + 16 * LDK;
+  auto consume = [&](const Group<D> &cur, int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < Group<D>::NC; ++u) {
+      const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *(u32x4 *)(ks + row * LDK + col) = cur.k[u];
+      *(u32x4 *)(vs + row * LD + col) = cur.v[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // S^T = K Q^T: A fragment = row t, dims 32kk + 8G .. +7.
+    f32x4 s = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8 *)(ks + t * LDK + 32 * kk + 8 * G), qf[kk], s, 0,
+                                                   0, 0);
+    // ---- online softmax per head column (rows r0 + 4G + jj) ----------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      s[jj] = (r0 + 4 * G + jj < sr.count) ? s[jj] : -INFINITY;
+      mx = fmaxf(mx, s[jj]);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float m_new = mx * p.scale_log2 + bias;
+    if (__any(m_new > m_run + kTau)) {
+      const float mr = fmaxf(m_run, m_new);
+      const float f = fast_exp2(m_run - mr);
+      l_run *= f;
+      m_run = mr;
+#pragma unroll
+      for (int c4 = 0; c4 < HC4; ++c4)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float fh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), 4 * c4 + ii));
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) acc[c4][hh][ii] *= fh;
+        }
+    }
+    const float nb = bias - m_run;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      s[jj] = fast_exp2(fmaf(s[jj], p.scale_log2, nb));
+      l_run += s[jj];
+    }
+    bf16x4 pb;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) pb[jj] = (bf16)s[jj];
+    const int2 pw = __builtin_bit_cast(int2, pb);
+    // ---- O += P V over the 4 row quads of the group --------------------------
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 vb[NH];
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const bf16 *src = vs + (4 * q + (t >> 2)) * LD + 16 * G + 64 * hh + 4 * (t & 3);
+        vb[hh] = as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src));
+      }
+#pragma unroll
+      for (int c4 = 0; c4 < HC4; ++c4) {
+        // P[head 4c4 + (lane & 3)][rows 4q..4q+3] lives in score lane 16q + 4c4 + (lane & 3).
+        const int src_lane = 16 * q + 4 * c4 + (lane & 3);
+        int2 a2;
+        a2.x = __builtin_amdgcn_ds_bpermute(4 * src_lane, pw.x);
+        a2.y = __builtin_amdgcn_ds_bpermute(4 * src_lane, pw.y);
+        const bf16x4 pa = __builtin_bit_cast(bf16x4, a2);
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) acc[c4][hh] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa, vb[hh], acc[c4][hh], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Rows are streamed in 16-row groups, wave w taking groups w, w+4, ...; one
+  // group's loads stay in flight while the previous group is consumed.
+  constexpr int kStep = 16 * kWaves;
+  Group<D> ring[kRing];
+#pragma unroll
+  for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, sr, 16 * wave + j * kStep, lane, i);
+  for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, sr, r0 + (j + kRing - 1) * kStep, lane, i);
+      if (r0 + j * kStep < sr.count) consume(ring[j], r0 + j * kStep);
+    }
+  }
+
+  // ---- per-head state (uniform), then merge the four waves pairwise --------
+  l_run += wave_shfl_xor(l_run, 16);
+  l_run += wave_shfl_xor(l_run, 32);
+  float m_h[NHD], l_h[NHD];
+#pragma unroll
+  for (int k = 0; k < NHD; ++k) {
+    m_h[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_run), k));
+    l_h[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_run), k));
+  }
+  auto publish = [&](int slot) __attribute__((always_inline)) {
+    f32x4 *A = (f32x4 *)(smem + slot * kSlotBytes);
+    float *ML = (float *)(A + HC4 * NH * 64);
+#pragma unroll
+    for (int c4 = 0; c4 < HC4; ++c4)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) A[(c4 * NH + hh) * 64 + lane] = acc[c4][hh];
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < NHD; ++k) {
+        ML[2 * k] = m_h[k];
+        ML[2 * k + 1] = l_h[k];
+      }
+    }
+  };
+  auto absorb = [&](int slot) __attribute__((always_inline)) {
+    const f32x4 *A = (const f32x4 *)(smem + slot * kSlotBytes);
+    const float *ML = (const float *)(A + HC4 * NH * 64);
+#pragma unroll
+    for (int c4 = 0; c4 < HC4; ++c4)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int k = 4 * c4 + ii;
+        const float m1 = ML[2 * k], l1 = ML[2 * k + 1];
+        const float mn = fmaxf(m_h[k], m1);
+        const float f0 = fast_exp2(m_h[k] - mn), f1 = fast_exp2(m1 - mn);
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) acc[c4][hh][ii] = acc[c4][hh][ii] * f0 + A[(c4 * NH + hh) * 64 + lane][ii] * f1;
+        l_h[k] = l_h[k] * f0 + l1 * f1;
+        m_h[k] = mn;
+      }
+  };
+  __syncthreads();                    // the V slabs are free
+  if (wave >= 2) publish(wave - 2);
+  __syncthreads();
+  if (wave < 2) absorb(wave);
+  __syncthreads();
+  if (wave == 1) publish(0);
+  __syncthreads();
+  if (wave != 0) return;
+  absorb(0);
+  // ---- write this split's partial state: lane l holds dims l + 64hh ------------
+#pragma unroll
+  for (int c4 = 0; c4 < HC4; ++c4)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int hd = 16 * hc + 4 * c4 + ii;
+      if (hd >= p.grp) continue;
+      float *wp = p.ws + (((size_t)b * p.Hq + g * p.grp + hd) * p.nsplit + split) * ws_stride<D>();
+      if (lane == 0) {
+        wp[0] = len_ok ? m_h[4 * c4 + ii] : NAN;
+        wp[1] = l_h[4 * c4 + ii];
+      }
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) wp[4 + lane + 64 * hh] = acc[c4][hh][ii];
+    }
+}
+
 // Merge the split partials of one (sequence, query head) and normalise: one
 // thread per output dimension, an online log-sum-exp merge over the splits.
 template <typename T, int D>
@@ -351,7 +572,15 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   p.grp = a.Hq / a.Hkv;
   p.hchunks = (p.grp + 15) / 16;
   p.scale_log2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(p.nsplit, a.Hkv * p.hchunks, a.B), dim3(256), 0, s, p);
+  const dim3 grid(p.nsplit, a.Hkv * p.hchunks, a.B);
+  if constexpr (sizeof(T) == 2) {
+    const int heads = p.grp < 16 ? p.grp : 16;   // heads per workgroup
+    if (heads <= 4) hipLaunchKernelGGL((decode_bf16_kernel<D, 1>), grid, dim3(256), 0, s, p);
+    else if (heads <= 8) hipLaunchKernelGGL((decode_bf16_kernel<D, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_bf16_kernel<D, 4>), grid, dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<T, D>), grid, dim3(256), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(D), 0, s, p);

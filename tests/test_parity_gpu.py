@@ -167,6 +167,10 @@ DECODE_CASES = [
              seed=65),
     Workload("dec_gqa32_bf16", "pi", "bf16", 1, 32, 1, 400, 64, k_win=50, pi=64, M=3,
              decode=True, seed=66),
+    Workload("dec_gqa8_bf16", "pi", "bf16", 2, 16, 2, 900, 128, k_win=80, pi=100, M=6,
+             decode=True, seed=69),
+    Workload("dec_gqa12_bf16", "window", "bf16", 1, 12, 1, 600, 128, k_win=300, decode=True,
+             seed=70),
 ]
 
 
