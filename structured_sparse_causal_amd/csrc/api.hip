@@ -188,20 +188,20 @@ int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *al
   return SA_OK;
 }
 
-// Decode split plan: the window range (at most k_win+1 rows, 2*seg for ECP,
-// never more than Lmax) is cut into splits of about 256 rows (a multiple of 64,
-// the rows one pass of a 4-wave workgroup covers); skip keys get one more split.
+// Decode split plan: the window rows below the query (at most k_win, or
+// 2*seg - 1 for ECP, never more than Lmax - 1) are cut into splits of about 256
+// rows (a multiple of 64, the rows one pass of a 4-wave workgroup covers); one
+// more split holds the query row and the skip keys.
 static void decode_plan(int Lmax, int mode, int k_win, int pi, int M, int seg, int *n_wsplit, int *chunk,
-                        int *has_skip, int *m_min) {
+                        int *m_min) {
   long long range = mode == SA_MODE_ECP ? 2LL * seg : (long long)k_win + 1;
   if (range > Lmax) range = Lmax;
-  int n = (int)((range + 255) / 256);
-  if (n < 1) n = 1;
-  long long c = (range + n - 1) / n;
+  const long long below = range - 1;
+  const int n = (int)((below + 255) / 256);
+  long long c = n > 0 ? (below + n - 1) / n : 64;
   c = (c + 63) / 64 * 64;
   *n_wsplit = n;
   *chunk = (int)c;
-  *has_skip = has_skips(mode, k_win, pi, M, Lmax) ? 1 : 0;
   *m_min = (mode == SA_MODE_PI && pi > 0) ? (int)(skip_m_min(k_win, pi) < (1LL << 30) ? skip_m_min(k_win, pi) : (1LL << 30)) : 1;
 }
 
@@ -210,9 +210,9 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d
   if (check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv != 0 ||
       check_mode(mode, k_win, pi, M, seg) != SA_OK)
     return 0;
-  int nw, chunk, hs, mm;
-  decode_plan(Lmax, mode, k_win, pi, M, seg, &nw, &chunk, &hs, &mm);
-  return round_up((size_t)B * Hq * (nw + hs) * (d + 4) * sizeof(float), 256);
+  int nw, chunk, mm;
+  decode_plan(Lmax, mode, k_win, pi, M, seg, &nw, &chunk, &mm);
+  return round_up((size_t)B * Hq * (nw + 1) * (d + 4) * sizeof(float), 256);
 }
 
 int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,
@@ -248,8 +248,8 @@ int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, 
   da.ws = (float *)workspace;
   da.B = B; da.Hq = Hq; da.Hkv = Hkv; da.Lmax = Lmax; da.d = d; da.dtype = dtype;
   da.mode = mode; da.k_win = k_win; da.pi = pi; da.M = M; da.seg = seg;
-  decode_plan(Lmax, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.has_skip, &da.m_min);
-  da.nsplit = da.n_wsplit + da.has_skip;
+  decode_plan(Lmax, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.m_min);
+  da.nsplit = da.n_wsplit + 1;
   hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   return SA_OK;

@@ -12,16 +12,14 @@
 // unnormalised accumulator) per query head; a combine kernel merges the splits
 // exactly (log-sum-exp merge) and normalises.
 //
-// Per wave and 16 rows: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows are the
-// A operand, loaded straight from HBM in operand layout; queries of the group
-// are the columns), online softmax per head column, then O^T += V^T P^T on
-// v_mfma_f32_16x16x16bf16_1k with the V^T fragment read transposed from a
-// per-wave LDS slab (ds_read_b64_tr_b16).  Each wave keeps one 16-row group
-// in flight while it consumes the previous one (kRing = 2 register buffers:
-// a deeper ring costs occupancy and measured slower); the four waves' partial
-// states are merged pairwise through LDS at the end.
-#include <type_traits>
-
+// bf16: each wave streams 16-row groups (K and V in whole cache lines, with
+// non-temporal loads, one group in flight while the previous one is consumed),
+// stages them in a per-wave LDS slab, computes S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (query heads of the group as columns), runs the
+// online softmax per head, and accumulates O with v_mfma_f32_4x4x4bf16_1k
+// (4 query heads x 64 dims per instruction).  fp32 uses the 16x16x4 f32
+// product with operands read from memory.  The four waves' partial states are
+// merged pairwise through LDS at the end.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -52,30 +50,36 @@ __device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
 
 // Rows of this split: count and position of row r.
 struct SplitRows {
-  int count, base, step;  // position(r) = base + r*step: step 1 (window), -pi (skips)
-  bool skip;
-  __device__ __forceinline__ int pos(int r) const { return base + r * step; }
+  int count, base, step;  // window splits: position(r) = base + r (local keys)
+  int qrow;               // last split: row 0 is the query row qrow (local),
+  bool last;              // rows r >= 1 are skips at base + r*step, step = -pi
+  __device__ __forceinline__ int pos(int r) const { return (last && r == 0) ? qrow : base + r * step; }
+  __device__ __forceinline__ bool skip_row(int r) const { return last && r != 0; }
 };
 
+// Rows of split `split` for the query at position i.  The window rows below i
+// are cut into n_wsplit splits of `chunk` rows; the last split holds the query
+// row itself and the skip keys i - m*pi (m = m_min..M, >= 0, all below the
+// window), so no split is nearly empty.
 __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int split) {
   SplitRows sr;
   const int lo = key_lo(i, p.mode, p.k_win, p.seg);
+  sr.qrow = i;
   if (split < p.n_wsplit) {
     const int a = lo + split * p.chunk;
-    const int e = min(a + p.chunk, i + 1);
+    const int e = min(a + p.chunk, i);
     sr.count = e > a ? e - a : 0;
     sr.base = a;
     sr.step = 1;
-    sr.skip = false;
+    sr.last = false;
   } else {
-    // Skip keys i - m*pi, m = m_min..M, that are >= 0 (all lie below lo).
     const int first = i - p.m_min * p.pi;
     int cnt = 0;
     if (p.mode == kModePi && p.M >= p.m_min && first >= 0) cnt = min(p.M - p.m_min, first / p.pi) + 1;
-    sr.count = cnt;
-    sr.base = first;
+    sr.count = 1 + cnt;
+    sr.base = first + p.pi;
     sr.step = -p.pi;
-    sr.skip = true;
+    sr.last = true;
   }
   return sr;
 }
@@ -119,17 +123,14 @@ __device__ __forceinline__ Group<D> load_group(const bf16 *Kp, const bf16 *Vp, c
 template <int D>
 constexpr int ws_stride() { return D + 4; }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
-  constexpr bool kBF = sizeof(T) == 2;
-  constexpr int LD = D + 8;
+// fp32 I/O: per wave and 16 rows, S^T = K Q^T on v_mfma_f32_16x16x4f32 and
+// O^T += V^T P^T on the same instruction, operands read straight from memory;
+// the four waves' partial states are merged pairwise through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(Params p) {
   constexpr int NDB = D / 16;
-  // LDS: per-wave V slabs while streaming rows, then two slots for the
-  // cross-wave merge (accumulators in C layout, max and sum per lane).
-  constexpr int kSlabBytes = kBF ? kWaves * 16 * LD * 2 : 0;
   constexpr int kSlotBytes = 64 * NDB * 16 + 2 * 64 * 4;
-  constexpr int kSmem = kSlabBytes > 2 * kSlotBytes ? kSlabBytes : 2 * kSlotBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ __attribute__((aligned(16))) char smem[2 * kSlotBytes];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = lane >> 4, t = lane & 15;
@@ -143,28 +144,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const bool hvalid = head < p.grp;
   const int hq = g * p.grp + head;
   const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lmax * D;
-  const T *Kp = (const T *)p.kc + kvoff;
-  const T *Vp = (const T *)p.vc + kvoff;
-  const T *Qp = (const T *)p.q + ((size_t)b * p.Hq + hq) * D;
+  const float *Kp = (const float *)p.kc + kvoff;
+  const float *Vp = (const float *)p.vc + kvoff;
+  const float *Qp = (const float *)p.q + ((size_t)b * p.Hq + hq) * D;
 
   SplitRows sr = split_rows(p, i, split);
   if (!len_ok) sr.count = 0;
 
-  float bias = 0.f;
+  float bias_loc = 0.f, bias_skip = 0.f;   // log2 priors of local and skip keys
   if (p.mode == kModePi && p.alpha != nullptr && hvalid) {
     const float a = p.alpha[(size_t)b * p.Hq + hq];
-    bias = sr.skip ? __log2f(1.0f - a) : __log2f(a);
+    bias_loc = __log2f(a);
+    bias_skip = __log2f(1.0f - a);
   }
 
   // Query fragment (B operand): column t = query head of the group.
-  constexpr int NQF = kBF ? D / 32 : D / 4;
-  typedef typename std::conditional<kBF, bf16x8, float>::type QFrag;
-  QFrag qf[NQF];
+  constexpr int NQF = D / 4;
+  float qf[NQF];
 #pragma unroll
-  for (int kk = 0; kk < NQF; ++kk) {
-    if constexpr (kBF) qf[kk] = hvalid ? *(const bf16x8 *)(Qp + 32 * kk + 8 * G) : bf16x8{};
-    else qf[kk] = hvalid ? (float)Qp[4 * kk + G] : 0.f;
-  }
+  for (int kk = 0; kk < NQF; ++kk) qf[kk] = hvalid ? Qp[4 * kk + G] : 0.f;
 
   f32x4 acc[NDB];
 #pragma unroll
@@ -177,12 +175,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      s[jj] = (r0 + 4 * G + jj < sr.count) ? s[jj] : -INFINITY;
+      const int rr = r0 + 4 * G + jj;
+      s[jj] = rr < sr.count ? fmaf(s[jj], p.scale_log2, sr.skip_row(rr) ? bias_skip : bias_loc) : -INFINITY;
       mx = fmaxf(mx, s[jj]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    const float m_new = mx * p.scale_log2 + bias;
+    const float m_new = mx;
     if (__any(m_new > m_run + kTau)) {
       const float mr = fmaxf(m_run, m_new);
       const float f = fast_exp2(m_run - mr);
@@ -191,79 +190,34 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
       for (int db = 0; db < NDB; ++db) acc[db] *= f;
       m_run = mr;
     }
-    const float nb = bias - m_run;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      s[jj] = fast_exp2(fmaf(s[jj], p.scale_log2, nb));
+      s[jj] = fast_exp2(s[jj] - m_run);
       l_run += s[jj];
     }
     return s;
   };
 
-  if constexpr (kBF) {
-    // Rows are streamed in 16-row groups, wave w taking groups w, w+4, ...;
-    // a ring of kRing groups keeps kRing - 1 groups of loads in flight while
-    // one is consumed (memory latency is hidden by bytes in flight per wave).
-    bf16 *vs = (bf16 *)smem + wave * 16 * LD;
-    auto consume = [&](const Group<D> &cur, int r0) {
-      f32x4 s = f32x4{};
+  for (int r0 = 16 * wave; r0 < sr.count; r0 += 16 * kWaves) {
+    const bool rvalid = r0 + t < sr.count;
+    const int prow = sr.pos(min(r0 + t, sr.count - 1));
+    f32x4 s = f32x4{};
 #pragma unroll
-      for (int kk = 0; kk < NQF; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[kk], qf[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < NQF; ++kk) {
+      const float a = rvalid ? (float)Kp[(size_t)prow * D + 4 * kk + G] : 0.f;
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[kk], s, 0, 0, 0);
+    }
+    s = softmax_step(s, r0);
+    // k index of the 16x16x4 f32 product = lane group G <-> row r0 + 4G + jj.
 #pragma unroll
-      for (int u = 0; u < Group<D>::NV; ++u) {
-        const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-        *(u32x4 *)(vs + row * LD + col) = cur.v[u];
-      }
-      s = softmax_step(s, r0);
-      bf16x4 pb;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) pb[jj] = (bf16)s[jj];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int jj = 0; jj < 4; ++jj) {
+      const int rr = r0 + 4 * G + jj;
+      const bool ok = rr < sr.count;
+      const size_t vrow = (size_t)sr.pos(ok ? rr : 0) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16 *src = vs + (4 * G + (t >> 2)) * LD + 16 * db + 4 * (t & 3);
-        const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(x), pb, acc[db], 0, 0, 0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    constexpr int kStep = 16 * kWaves;
-    Group<D> ring[kRing];
-#pragma unroll
-    for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, sr, 16 * wave + j * kStep, lane, i);
-    for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
-#pragma unroll
-      for (int j = 0; j < kRing; ++j) {
-        ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, sr, r0 + (j + kRing - 1) * kStep, lane, i);
-        if (r0 + j * kStep < sr.count) consume(ring[j], r0 + j * kStep);
-      }
-    }
-  } else {
-    for (int r0 = 16 * wave; r0 < sr.count; r0 += 16 * kWaves) {
-      const bool rvalid = r0 + t < sr.count;
-      const int prow = sr.pos(min(r0 + t, sr.count - 1));
-      f32x4 s = f32x4{};
-#pragma unroll
-      for (int kk = 0; kk < NQF; ++kk) {
-        const float a = rvalid ? (float)Kp[(size_t)prow * D + 4 * kk + G] : 0.f;
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[kk], s, 0, 0, 0);
-      }
-      s = softmax_step(s, r0);
-      // k index of the 16x16x4 f32 product = lane group G <-> row r0 + 4G + jj.
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rr = r0 + 4 * G + jj;
-        const bool ok = rr < sr.count;
-        const size_t vrow = (size_t)sr.pos(ok ? rr : 0) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const float a = ok ? (float)Vp[vrow + 16 * db + t] : 0.f;
-          acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[jj], acc[db], 0, 0, 0);
-        }
+        const float a = ok ? (float)Vp[vrow + 16 * db + t] : 0.f;
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[jj], acc[db], 0, 0, 0);
       }
     }
   }
@@ -291,7 +245,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     l_run = l_run * f0 + l1 * f1;
     m_run = mn;
   };
-  __syncthreads();                    // the V slabs are free
+  __syncthreads();                    // every wave is done streaming
   if (wave >= 2) publish(wave - 2);
   __syncthreads();
   if (wave < 2) absorb(wave);
@@ -360,10 +314,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   SplitRows sr = split_rows(p, i, split);
   if (!len_ok) sr.count = 0;
 
-  float bias = 0.f;
+  float bias_loc = 0.f, bias_skip = 0.f;   // log2 priors of local and skip keys
   if (p.mode == kModePi && p.alpha != nullptr && hvalid) {
     const float a = p.alpha[(size_t)b * p.Hq + hq];
-    bias = sr.skip ? __log2f(1.0f - a) : __log2f(a);
+    bias_loc = __log2f(a);
+    bias_skip = __log2f(1.0f - a);
   }
 
   bf16x8 qf[NQF];
@@ -399,12 +354,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      s[jj] = (r0 + 4 * G + jj < sr.count) ? s[jj] : -INFINITY;
+      const int rr = r0 + 4 * G + jj;
+      s[jj] = rr < sr.count ? fmaf(s[jj], p.scale_log2, sr.skip_row(rr) ? bias_skip : bias_loc) : -INFINITY;
       mx = fmaxf(mx, s[jj]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    const float m_new = mx * p.scale_log2 + bias;
+    const float m_new = mx;
     if (__any(m_new > m_run + kTau)) {
       const float mr = fmaxf(m_run, m_new);
       const float f = fast_exp2(m_run - mr);
@@ -419,10 +375,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
           for (int hh = 0; hh < NH; ++hh) acc[c4][hh][ii] *= fh;
         }
     }
-    const float nb = bias - m_run;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      s[jj] = fast_exp2(fmaf(s[jj], p.scale_log2, nb));
+      s[jj] = fast_exp2(s[jj] - m_run);
       l_run += s[jj];
     }
     bf16x4 pb;
@@ -579,7 +534,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
     else if (heads <= 8) hipLaunchKernelGGL((decode_bf16_kernel<D, 2>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((decode_bf16_kernel<D, 4>), grid, dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

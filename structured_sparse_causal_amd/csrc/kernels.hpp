@@ -42,7 +42,7 @@ struct DecodeArgs {
   float *ws;            // [B*Hq][nsplit][d+4]: max, sum, 2 pad, accumulator
   int B, Hq, Hkv, Lmax, d, dtype;
   int mode, k_win, pi, M, seg, m_min;
-  int n_wsplit, chunk, has_skip, nsplit;
+  int n_wsplit, chunk, nsplit;   // window splits, rows per window split, n_wsplit + 1
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

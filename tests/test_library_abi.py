@@ -120,10 +120,12 @@ def test_decode_rejects(lib, kw, code):
 
 def test_decode_workspace_size(lib):
     ws = lib.sparse_attn_decode_workspace_size
-    # 2049 window rows -> 9 splits of 256, plus one split for the skip keys.
-    assert ws(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0) == 64 * 32 * 10 * 132 * 4
+    # 2048 window rows below the query -> 8 splits of 256, plus one split for the
+    # query row and the skip keys.
+    assert ws(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0) == 64 * 32 * 9 * 132 * 4
     assert ws(64, 32, 8, 32768, 128, BF16, WINDOW, 2048, 0, 0, 0) == 64 * 32 * 9 * 132 * 4
-    assert ws(1, 1, 1, 100, 64, F32, ECP, 0, 0, 0, 512) == 256 * ((1 * 1 * 1 * 68 * 4 + 255) // 256)
+    assert ws(1, 1, 1, 100, 64, F32, ECP, 0, 0, 0, 512) == 256 * ((1 * 1 * 2 * 68 * 4 + 255) // 256)
+    assert ws(2, 2, 2, 300, 64, BF16, WINDOW, 0, 0, 0, 0) == 256 * ((2 * 2 * 1 * 68 * 4 + 255) // 256)  # k = 0
     assert ws(1, 1, 1, 100, 60, F32, ECP, 0, 0, 0, 512) == 0
 
 

@@ -171,6 +171,9 @@ DECODE_CASES = [
              decode=True, seed=69),
     Workload("dec_gqa12_bf16", "window", "bf16", 1, 12, 1, 600, 128, k_win=300, decode=True,
              seed=70),
+    Workload("dec_k0_bf16", "window", "bf16", 2, 4, 2, 300, 64, k_win=0, decode=True, seed=72),
+    Workload("dec_k0_pi_f32", "pi", "f32", 2, 2, 1, 300, 64, k_win=0, pi=37, M=5, decode=True,
+             seed=73),
 ]
 
 
