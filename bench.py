@@ -257,6 +257,8 @@ def main():
     ap.add_argument("--workload", default="ecp_bf16")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, metavar="WORKLOAD",
+                    help="time one workload of the hot path and print its statistics only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -277,6 +279,11 @@ def main():
         return
     sa.load_library()
     dev = torch.device("cuda:0")
+    if args.only is not None:
+        wx = WORKLOADS[args.only]
+        run = run_decode_workload if wx.decode else run_prefill_workload
+        print(json.dumps({"workload": wx.name, **run(torch, sa, wx, args.steps, args.warmup)}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     if w.decode:
         raise SystemExit("the headline workload must be a prefill workload")
@@ -313,7 +320,7 @@ def main():
     # Dominant kernel: per-launch durations from HIP events on the launch stream.
     t_ev = event_times(torch, step, args.steps)
     kern_ms = float(np.mean(t_ev)) / (w.loops if w.loops > 1 else 1)
-    dominant = "prefill_kernel<bf16,%d>" % w.d
+    dominant = "prefill_bf16_kernel<%d>" % w.d
     achieved = flop / (kern_ms * 1e-3) / 1e12
     ai = flop / nb
     bound = "mfma" if ai * HBM_PEAK_GBS / 1000.0 >= MFMA_BF16_PEAK_TFLOPS else "hbm"

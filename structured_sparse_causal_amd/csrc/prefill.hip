@@ -44,6 +44,7 @@ struct Params {
   const void *skip_acc;
   int N, Hq, Hkv, mode, k_win, seg, nqb, total, skip_first;
   int heads_per_xcd;   // > 0: heavy-first block order per XCD (see block_of)
+  int rank_group;      // heads walked together in rank order (divides heads_per_xcd)
   int ecp_J, ecp_C;    // ECP blocks per half-segment and half-segments (0: none)
   float scale_log2;
 };
@@ -62,10 +63,11 @@ __device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
 // light, causal window blocks near position 0 are light.  Blocks are handed
 // out heaviest first, so the light ones fill the grid's tail (list scheduling
 // by decreasing cost).  The grid is split into 8 contiguous ranges, one per
-// XCD (xcd_remap); each XCD owns heads_per_xcd whole heads (their K/V stay
-// in its L2) and walks them in cost rank order: all heads' heaviest blocks,
-// then the next, and so on.  Otherwise (heads not a multiple of 8, or block
-// costs nearly equal) each head's blocks run last-to-first.
+// XCD (xcd_remap); each XCD owns heads_per_xcd whole heads and walks them in
+// groups of rank_group heads whose K/V fit in its L2, each group in cost rank
+// order: all the group's heaviest blocks, then the next, and so on.
+// Otherwise (heads not a multiple of 8, or block costs nearly equal) each
+// head's blocks run last-to-first.
 struct BlockId {
   int bh, qb;
 };
@@ -80,8 +82,10 @@ __device__ __forceinline__ BlockId block_of(const Params &p, int bid) {
   }
   const int per = p.total / 8;
   const int x = logical / per, idx = logical - x * per;
-  const int rank = idx / p.heads_per_xcd;
-  r.bh = x * p.heads_per_xcd + (idx - rank * p.heads_per_xcd);
+  const int gsz = p.rank_group * p.nqb;                 // blocks of one head group
+  const int grp = idx / gsz, rem = idx - grp * gsz;
+  const int rank = rem / p.rank_group;
+  r.bh = x * p.heads_per_xcd + grp * p.rank_group + (rem - rank * p.rank_group);
   if (p.ecp_J > 0) {
     // ECP with whole half-segments: cost depends on the block's position j in
     // its half-segment (heavier later) and on c > 0.
@@ -517,6 +521,19 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   const int BH = a.B * a.Hq;
   const bool uneven = a.mode == kModeEcp || (long long)a.k_win * 4 >= a.N;
   p.heads_per_xcd = (uneven && BH % 8 == 0) ? BH / 8 : 0;
+  // Heads of one rank walk: as many as keep their K and V within about 3 MB
+  // (the XCD's L2 is 4 MB), and a divisor of heads_per_xcd.  Walking all of an
+  // XCD's heads at once balances slightly better but re-reads K/V from HBM
+  // (measured 2.1x the algorithmic fetch for ECP, against 0.96x with groups).
+  p.rank_group = 1;
+  if (p.heads_per_xcd > 0) {
+    const long long kv_head = 2LL * a.N * D * (long long)sizeof(T) / (a.Hq / a.Hkv);  // K+V share per query head
+    for (int gsz = p.heads_per_xcd; gsz >= 1; --gsz)
+      if (p.heads_per_xcd % gsz == 0 && gsz * kv_head <= (3LL << 20)) {
+        p.rank_group = gsz;
+        break;
+      }
+  }
   p.ecp_J = p.ecp_C = 0;
   if (a.mode == kModeEcp && a.seg % BM == 0 && a.N % a.seg == 0) {
     p.ecp_J = a.seg / BM;
