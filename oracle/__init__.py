@@ -72,6 +72,12 @@ def _load():
             lib.orc_decode.restype = i32
             lib.orc_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                        i32, i64, i64, i64, i64, vp]
+            lib.orc_lse_rows.restype = i32
+            lib.orc_lse_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64,
+                                         i32, i64, i64, i64, i64, vp, i64, vp]
+            lib.orc_bwd.restype = i32
+            lib.orc_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                    i32, i64, i64, i64, i64, vp, vp, vp, vp]
             lib.orc_num_threads.restype = i32
             lib.orc_set_num_threads.argtypes = [i32]
             _lib = lib
@@ -153,6 +159,57 @@ def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
                           sel_p, nsel, out.ctypes.data)
     _check(rc)
     return out
+
+
+def lse(q, k, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
+        rows=None) -> np.ndarray:
+    """Log-sum-exp of each row's scores (natural log), fp64: [B,Hq,N], or
+    [len(rows)] for flat row ids."""
+    lib = _load()
+    q32, k32 = _f32(q), _f32(k)
+    B, Hq, N, d = q32.shape
+    Hkv = k32.shape[1]
+    if k32.shape != (B, Hkv, N, d):
+        raise ValueError("oracle: k shape mismatch")
+    a32 = _f32(alpha) if alpha is not None else None
+    if rows is None:
+        out = np.empty((B, Hq, N), dtype=np.float64)
+        sel_p, nsel = None, 0
+    else:
+        sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
+        out = np.empty(sel.size, dtype=np.float64)
+        sel_p, nsel = sel.ctypes.data, sel.size
+    rc = lib.orc_lse_rows(q32.ctypes.data, k32.ctypes.data,
+                          a32.ctypes.data if a32 is not None else None,
+                          B, Hq, Hkv, N, d, _mode(mode), int(k_win), int(pi), int(M), int(seg),
+                          sel_p, nsel, out.ctypes.data)
+    _check(rc)
+    return out
+
+
+def bwd(q, k, v, alpha, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0):
+    """Backward pass in fp64 (the chain rule through the forward definition;
+    the gate gradient follows pi-Attention section 2 item 3).
+    Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d], dalpha [B,Hq,N] or None)."""
+    lib = _load()
+    q32, k32, v32, do32 = _f32(q), _f32(k), _f32(v), _f32(dO)
+    B, Hq, N, d = q32.shape
+    Hkv = k32.shape[1]
+    if k32.shape != (B, Hkv, N, d) or v32.shape != k32.shape or do32.shape != q32.shape:
+        raise ValueError("oracle: shape mismatch")
+    m = _mode(mode)
+    a32 = _f32(alpha) if alpha is not None else None
+    dq = np.empty((B, Hq, N, d), dtype=np.float64)
+    dk = np.empty((B, Hkv, N, d), dtype=np.float64)
+    dv = np.empty((B, Hkv, N, d), dtype=np.float64)
+    da = np.zeros((B, Hq, N), dtype=np.float64) if m == MODES["pi"] else None
+    rc = lib.orc_bwd(q32.ctypes.data, k32.ctypes.data, v32.ctypes.data,
+                     a32.ctypes.data if a32 is not None else None, do32.ctypes.data,
+                     B, Hq, Hkv, N, d, m, int(k_win), int(pi), int(M), int(seg),
+                     dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                     da.ctypes.data if da is not None else None)
+    _check(rc)
+    return dq, dk, dv, da
 
 
 def decode(q, k_cache, v_cache, lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,

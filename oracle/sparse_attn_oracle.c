@@ -1,6 +1,6 @@
 /*
  * sparse_attn_oracle.c -- plain fp64 CPU oracle for causal structured-sparse
- * attention (forward and single-token decode).
+ * attention (forward, its log-sum-exp, backward, and single-token decode).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the tests, the smoke check and the CPU-baseline leg of
@@ -267,6 +267,174 @@ int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *
         free(keys);
         free(labels);
         free(score);
+    }
+    return err;
+}
+
+/*
+ * Log-sum-exp of the scores of selected rows (natural log units): the
+ * softmax normaliser a training forward keeps for the backward pass,
+ *   lse_i = log sum_{j in K(i)} exp(score(i, j)).
+ *   sel/nsel as for orc_fwd_rows; out[nsel] doubles.
+ */
+int orc_lse_rows(const float *q, const float *k, const float *alpha,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                 const int64_t *sel, int64_t nsel, double *out)
+{
+    int64_t cap, total, r;
+    int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
+    if (err != ORC_OK || N <= 0) return ORC_ERR_ARGS;
+    total = B * Hq * N;
+    if (sel == NULL) nsel = total;
+    cap = orc_key_capacity(mode, k_win, M, seg);
+    err = ORC_OK;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc((size_t)cap * sizeof(int64_t));
+        int32_t *labels = (int32_t *)malloc((size_t)cap * sizeof(int32_t));
+        int local_err = (keys && labels) ? ORC_OK : ORC_ERR_NOMEM;
+        const double inv_sqrt_d = 1.0 / sqrt((double)d);
+#pragma omp for schedule(dynamic, 64)
+        for (r = 0; r < nsel; ++r) {
+            int64_t row = sel ? sel[r] : r, b, h, i, g, n, t, c;
+            double lp, ls, mx = -INFINITY, sum = 0.0;
+            const float *qrow, *kmat;
+            if (local_err != ORC_OK) continue;
+            if (row < 0 || row >= total) { local_err = ORC_ERR_ARGS; continue; }
+            i = row % N;
+            h = (row / N) % Hq;
+            b = row / (N * Hq);
+            g = h / (Hq / Hkv);
+            if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) continue;
+            n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+            if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
+            qrow = q + row * d;
+            kmat = k + (b * Hkv + g) * N * d;
+            for (t = 0; t < n; ++t) {
+                double dot = 0.0, sc;
+                for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)kmat[keys[t] * d + c];
+                sc = dot * inv_sqrt_d + (labels[t] == ORC_LOCAL ? lp : ls);
+                if (sc > mx) mx = sc;
+            }
+            for (t = 0; t < n; ++t) {
+                double dot = 0.0;
+                for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)kmat[keys[t] * d + c];
+                sum += exp(dot * inv_sqrt_d + (labels[t] == ORC_LOCAL ? lp : ls) - mx);
+            }
+            out[r] = mx + log(sum);
+        }
+        if (local_err != ORC_OK) {
+#pragma omp critical
+            err = local_err;
+        }
+        free(keys);
+        free(labels);
+    }
+    return err;
+}
+
+/*
+ * Backward pass: gradients of a scalar loss L given dO = dL/dO, by the chain
+ * rule through the definition above.  For every row (b, h, i), with
+ * P_ij = softmax over K(i) of score(i, j):
+ *   dP_ij   = <dO_i, v_j>
+ *   D_i     = sum_j P_ij dP_ij
+ *   dS_ij   = P_ij (dP_ij - D_i)              (dL / d score(i, j))
+ *   dq_i    = sum_j dS_ij k_j / sqrt(d)
+ *   dk_j   += dS_ij q_i / sqrt(d)             (over all rows and the GQA group)
+ *   dv_j   += P_ij dO_i
+ *   dalpha_i = sum_{j local} dS_ij / alpha_i - sum_{j skip} dS_ij / (1 - alpha_i)
+ * (d score / d alpha is 1/alpha on local keys and -1/(1-alpha) on skip keys,
+ * pi-Attention section 2 item 3).  The skip term is formed as
+ * exp(score without prior - lse_i) (dP_ij - D_i), which equals
+ * dS_ij / (1 - alpha_i) and stays finite at alpha = 1.
+ *   dO [B, Hq, N, d] fp32;  dq [B, Hq, N, d], dk, dv [B, Hkv, N, d] doubles;
+ *   dalpha [B, Hq, N] doubles or NULL (PI only).
+ * Work is split over (batch, KV head): one thread owns the dk/dv rows of a
+ * KV head and every query row of its group.
+ */
+int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, const float *dO,
+            int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+            int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+            double *dq, double *dk, double *dv, double *dalpha)
+{
+    int64_t cap, u;
+    int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
+    if (err != ORC_OK || N <= 0) return ORC_ERR_ARGS;
+    cap = orc_key_capacity(mode, k_win, M, seg);
+    err = ORC_OK;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc((size_t)cap * sizeof(int64_t));
+        int32_t *labels = (int32_t *)malloc((size_t)cap * sizeof(int32_t));
+        double *sc = (double *)malloc((size_t)cap * sizeof(double));
+        double *pr = (double *)malloc((size_t)cap * sizeof(double));
+        double *dp = (double *)malloc((size_t)cap * sizeof(double));
+        int local_err = (keys && labels && sc && pr && dp) ? ORC_OK : ORC_ERR_NOMEM;
+        const double inv_sqrt_d = 1.0 / sqrt((double)d);
+#pragma omp for schedule(dynamic, 1)
+        for (u = 0; u < B * Hkv; ++u) {
+            const int64_t b = u / Hkv, g = u % Hkv, grp = Hq / Hkv;
+            const float *kmat = k + u * N * d, *vmat = v + u * N * d;
+            double *dkm = dk + u * N * d, *dvm = dv + u * N * d;
+            int64_t hh, i, t, c, n;
+            if (local_err != ORC_OK) continue;
+            for (t = 0; t < N * d; ++t) { dkm[t] = 0.0; dvm[t] = 0.0; }
+            for (hh = 0; hh < grp && local_err == ORC_OK; ++hh) {
+                const int64_t h = g * grp + hh;
+                for (i = 0; i < N; ++i) {
+                    const int64_t row = (b * Hq + h) * N + i;
+                    const float *qrow = q + row * d, *dorow = dO + row * d;
+                    double lp, ls, mx = -INFINITY, sum = 0.0, lse, D = 0.0, da = 0.0;
+                    if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) break;
+                    n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+                    if (n <= 0) { local_err = ORC_ERR_ARGS; break; }
+                    for (t = 0; t < n; ++t) {
+                        double dot = 0.0;
+                        for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)kmat[keys[t] * d + c];
+                        sc[t] = dot * inv_sqrt_d;   /* without prior */
+                        {
+                            const double full = sc[t] + (labels[t] == ORC_LOCAL ? lp : ls);
+                            if (full > mx) mx = full;
+                        }
+                    }
+                    for (t = 0; t < n; ++t) sum += exp(sc[t] + (labels[t] == ORC_LOCAL ? lp : ls) - mx);
+                    lse = mx + log(sum);
+                    for (t = 0; t < n; ++t) {
+                        double dot = 0.0;
+                        pr[t] = exp(sc[t] + (labels[t] == ORC_LOCAL ? lp : ls) - lse);
+                        for (c = 0; c < d; ++c) dot += (double)dorow[c] * (double)vmat[keys[t] * d + c];
+                        dp[t] = dot;
+                        D += pr[t] * dot;
+                    }
+                    for (c = 0; c < d; ++c) dq[row * d + c] = 0.0;
+                    for (t = 0; t < n; ++t) {
+                        const double ds = pr[t] * (dp[t] - D);
+                        const int64_t j = keys[t];
+                        for (c = 0; c < d; ++c) {
+                            dq[row * d + c] += ds * (double)kmat[j * d + c] * inv_sqrt_d;
+                            dkm[j * d + c] += ds * (double)qrow[c] * inv_sqrt_d;
+                            dvm[j * d + c] += pr[t] * (double)dorow[c];
+                        }
+                        if (mode == ORC_MODE_PI) {
+                            if (labels[t] == ORC_LOCAL) da += ds / (double)alpha[row];
+                            else da -= exp(sc[t] - lse) * (dp[t] - D);
+                        }
+                    }
+                    if (dalpha != NULL) dalpha[row] = da;
+                }
+            }
+        }
+        if (local_err != ORC_OK) {
+#pragma omp critical
+            err = local_err;
+        }
+        free(keys);
+        free(labels);
+        free(sc);
+        free(pr);
+        free(dp);
     }
     return err;
 }
