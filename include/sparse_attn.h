@@ -103,6 +103,50 @@ int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *al
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training forward: sparse_attn_fwd (same arguments, workspace and errors)
+ * that also writes the log-sum-exp of every row's scores,
+ *   lse[b, h, i] = log sum_{j in K(i)} exp(<q_i, k_j>/sqrt(d) + prior(i, j)),
+ * fp32 [B, Hq, N], natural log; the backward pass reads it.  lse must not be
+ * NULL nor overlap another tensor.
+ */
+int sparse_attn_fwd_lse(const void *q, const void *k, const void *v, const float *alpha, void *o,
+                        float *lse, int B, int Hq, int Hkv, int N, int d, int dtype,
+                        int mode, int k_win, int pi, int M, int seg,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace sparse_attn_bwd needs (0 for arguments it would
+ * reject, including dtype != SA_DTYPE_BF16).
+ */
+size_t sparse_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype,
+                                      int mode, int k_win, int pi, int M, int seg);
+
+/*
+ * Backward pass: gradients of a scalar loss L given dO = dL/dO, through the
+ * forward's single softmax over each key set with the gate as a log-prior
+ * (pi-Attention section 2 item 3 for the gate):
+ *   dq [B,Hq,N,d], dk and dv [B,Hkv,N,d] (bf16; dk, dv summed over the query
+ *   heads of each GQA group), dalpha [B,Hq,N] fp32 (PI mode when alpha is
+ *   given; may be NULL otherwise) with
+ *   dL/dalpha_i = sum_{j local} dS_ij / alpha_i - sum_{j skip} dS_ij / (1 - alpha_i),
+ *   dS_ij = P_ij (<dO_i, v_j> - <dO_i, o_i>) the gradient of score (i, j);
+ *   as sum_j dS_ij = 0, it is computed as -sum_{j skip} dS_ij / (alpha_i (1 - alpha_i))
+ *   (0 on rows without skip keys, finite at alpha_i = 1).
+ *   o, lse: the outputs of sparse_attn_fwd_lse for the same q, k, v, alpha.
+ *   bf16 I/O only (SA_ERR_UNSUPPORTED otherwise); d in {64, 128}.  No output
+ *   may overlap an input, another output or the workspace.
+ *   workspace: >= sparse_attn_bwd_workspace_size(...) bytes, 256-byte
+ *   aligned; scratch, not to be shared by concurrent calls.
+ * Returns SA_OK or an error code.
+ */
+int sparse_attn_bwd(const void *q, const void *k, const void *v, const float *alpha,
+                    const void *o, const float *lse, const void *dO,
+                    void *dq, void *dk, void *dv, float *dalpha,
+                    int B, int Hq, int Hkv, int N, int d, int dtype,
+                    int mode, int k_win, int pi, int M, int seg,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace sparse_attn_decode needs (never 0 for valid
  * arguments; 0 for arguments sparse_attn_decode would reject).
  */

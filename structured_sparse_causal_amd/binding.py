@@ -29,7 +29,8 @@ _LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 _lock = threading.Lock()
 _lib = None
 
-EXPORTED = ("sparse_attn_fwd_workspace_size", "sparse_attn_fwd",
+EXPORTED = ("sparse_attn_fwd_workspace_size", "sparse_attn_fwd", "sparse_attn_fwd_lse",
+            "sparse_attn_bwd_workspace_size", "sparse_attn_bwd",
             "sparse_attn_decode_workspace_size", "sparse_attn_decode",
             "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_version")
 
@@ -57,6 +58,12 @@ def load_library():
         lib.sparse_attn_fwd_workspace_size.argtypes = [i] * 11
         lib.sparse_attn_fwd.restype = i
         lib.sparse_attn_fwd.argtypes = [vp] * 5 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_fwd_lse.restype = i
+        lib.sparse_attn_fwd_lse.argtypes = [vp] * 6 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_bwd_workspace_size.restype = sz
+        lib.sparse_attn_bwd_workspace_size.argtypes = [i] * 11
+        lib.sparse_attn_bwd.restype = i
+        lib.sparse_attn_bwd.argtypes = [vp] * 11 + [i] * 11 + [vp, sz, vp]
         lib.sparse_attn_decode_workspace_size.restype = sz
         lib.sparse_attn_decode_workspace_size.argtypes = [i] * 11
         lib.sparse_attn_decode.restype = i
@@ -128,9 +135,11 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
-        out=None, workspace=None):
+        out=None, workspace=None, lse=None):
     """Prefill forward: q [B,Hq,N,d], k/v [B,Hkv,N,d] (bf16 or fp32, on the
-    GPU), alpha [B,Hq,N] fp32 for the gated mode.  Returns o [B,Hq,N,d]."""
+    GPU), alpha [B,Hq,N] fp32 for the gated mode.  Returns o [B,Hq,N,d].
+    With ``lse`` (an fp32 [B,Hq,N] tensor) the row log-sum-exp is written
+    too (the training forward)."""
     lib = load_library()
     _need_gpu(q, k, v, alpha, out, workspace)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -153,12 +162,55 @@ def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, s
     dt = _DTYPES[q.dtype]
     nbytes = int(lib.sparse_attn_fwd_workspace_size(B, Hq, Hkv, N, d, dt, m, k_win, pi, M, seg))
     ws = _workspace(nbytes, q.device, workspace)
-    rc = lib.sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(out),
-                             B, Hq, Hkv, N, d, dt, m, int(k_win), int(pi), int(M), int(seg),
-                             _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
+    if lse is None:
+        rc = lib.sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(out),
+                                 B, Hq, Hkv, N, d, dt, m, int(k_win), int(pi), int(M), int(seg),
+                                 _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
+    else:
+        _need_gpu(lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
+        rc = lib.sparse_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(out), _ptr(lse),
+                                     B, Hq, Hkv, N, d, dt, m, int(k_win), int(pi), int(M), int(seg),
+                                     _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
     if rc != SA_OK:
         _raise(lib, rc, "sparse_attn_fwd")
     return out
+
+
+def bwd_workspace_size(B, Hq, Hkv, N, d, dtype, mode, k_win=0, pi=0, M=0, seg=0) -> int:
+    lib = load_library()
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.sparse_attn_bwd_workspace_size(B, Hq, Hkv, N, d, dt, _mode(mode), k_win, pi, M, seg))
+
+
+def bwd(q, k, v, alpha, o, lse, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
+        seg: int = 0, workspace=None):
+    """Backward pass (bf16): gradients given dO for the forward that produced
+    o and lse (``fwd(..., lse=...)``).  Returns (dq, dk, dv, dalpha); dalpha
+    is an fp32 [B,Hq,N] tensor for the gated mode with alpha, else None."""
+    lib = load_library()
+    _need_gpu(q, k, v, alpha, o, lse, dO, workspace)
+    if q.dtype != torch.bfloat16 or any(t.dtype != torch.bfloat16 for t in (k, v, o, dO)):
+        raise NotImplementedError("the backward pass takes bf16 q, k, v, o, dO")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or v.shape != k.shape or o.shape != q.shape or dO.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o, dO")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be fp32 [B, Hq, N]")
+    m = _mode(mode)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dalpha = torch.empty_like(alpha) if (alpha is not None and m == MODE_PI) else None
+    nbytes = int(lib.sparse_attn_bwd_workspace_size(B, Hq, Hkv, N, d, DTYPE_BF16, m, k_win, pi, M, seg))
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha),
+                             B, Hq, Hkv, N, d, DTYPE_BF16, m, int(k_win), int(pi), int(M), int(seg),
+                             _ptr(ws), nbytes, _stream(q.device))
+    if rc != SA_OK:
+        _raise(lib, rc, "sparse_attn_bwd")
+    return dq, dk, dv, dalpha
 
 
 def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.hip", "prefill.hip", "skip.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefill.hip", "skip.hip", "decode.hip", "backward.hip"]
 
 
 def hipcc() -> str:

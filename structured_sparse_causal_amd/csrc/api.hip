@@ -130,17 +130,28 @@ size_t sparse_attn_fwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int 
   return fwd_layout(fwd_chunk_heads(B, Hq, Hkv, N, d, dtype), N, d, dtype).total;
 }
 
-int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *alpha, void *o, int B, int Hq,
-                    int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, void *o, float *lse, int B, int Hq,
+             int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg, void *workspace,
+             size_t workspace_bytes, void *stream) {
   g_err[0] = 0;
   int rc = fwd_validate(q, k, v, alpha, o, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
   if (rc != SA_OK) return rc;
+  if (lse != nullptr) {
+    if (!aligned(lse, 4)) return fail(SA_ERR_INVALID, "misaligned lse");
+    const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype), nl = (size_t)B * Hq * N * sizeof(float);
+    if (overlap(lse, nl, q, nq) || overlap(lse, nl, o, nq) || overlap(lse, nl, k, (size_t)B * Hkv * N * d * elem_size(dtype)) ||
+        overlap(lse, nl, v, (size_t)B * Hkv * N * d * elem_size(dtype)) || overlap(lse, nl, alpha, alpha ? nl : 0))
+      return fail(SA_ERR_INVALID, "lse overlaps a tensor");
+  }
   const bool skips = has_skips(mode, k_win, pi, M, N);
   hipStream_t s = (hipStream_t)stream;
   sa::PrefillArgs pa;
   pa.q = q; pa.k = k; pa.v = v; pa.alpha = alpha; pa.o = o;
-  pa.skip_ml = nullptr; pa.skip_acc = nullptr;
+  pa.skip_ml = nullptr; pa.skip_acc = nullptr; pa.lse = lse;
   pa.B = B; pa.Hq = Hq; pa.Hkv = Hkv; pa.N = N; pa.d = d; pa.dtype = dtype;
   pa.mode = mode; pa.k_win = k_win; pa.seg = seg;
   pa.skip_first = N;
@@ -182,10 +193,56 @@ int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *al
     pc.skip_ml = sk.ml;
     pc.skip_acc = sk.acc;
     pc.skip_first = (int)(mm * pi);
+    pc.lse = lse != nullptr ? lse + (size_t)bh0 * N : nullptr;
     e = sa::launch_prefill(pc, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   }
   return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_fwd(const void *q, const void *k, const void *v, const float *alpha, void *o, int B, int Hq,
+                    int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, alpha, o, nullptr, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg, workspace,
+                  workspace_bytes, stream);
+}
+
+int sparse_attn_fwd_lse(const void *q, const void *k, const void *v, const float *alpha, void *o, float *lse,
+                        int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M,
+                        int seg, void *workspace, size_t workspace_bytes, void *stream) {
+  if (lse == nullptr) {
+    g_err[0] = 0;
+    return fail(SA_ERR_INVALID, "null lse pointer");
+  }
+  return fwd_impl(q, k, v, alpha, o, lse, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg, workspace,
+                  workspace_bytes, stream);
+}
+
+// Backward workspace: D_i and c_i per query row (+16 floats of padding for
+// the 16-byte vector loads at the tail), then, with skip keys, the skip-key
+// contributions in fp32: dq [rows][d], dk and dv [kv rows][d].
+struct BwdLayout {
+  size_t dv_off, cv_off, dqs_off, dks_off, dvs_off, total;
+};
+
+static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d, bool skips) {
+  BwdLayout L;
+  const size_t rows = (size_t)B * Hq * N, kvrows = (size_t)B * Hkv * N;
+  size_t at = 0;
+  L.dv_off = at; at += round_up((rows + 16) * sizeof(float), 256);
+  L.cv_off = at; at += round_up((rows + 16) * sizeof(float), 256);
+  L.dqs_off = L.dks_off = L.dvs_off = 0;
+  if (skips) {
+    L.dqs_off = at; at += round_up(rows * d * sizeof(float), 256);
+    L.dks_off = at; at += round_up(kvrows * d * sizeof(float), 256);
+    L.dvs_off = at; at += round_up(kvrows * d * sizeof(float), 256);
+  }
+  L.total = at;
+  return L;
 }
 
 // Decode split plan: the window rows below the query (at most k_win, or
@@ -251,6 +308,72 @@ int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, 
   decode_plan(Lmax, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.m_min);
   da.nsplit = da.n_wsplit + 1;
   hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+  return SA_OK;
+}
+
+size_t sparse_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win,
+                                      int pi, int M, int seg) {
+  if (dtype != SA_DTYPE_BF16 || check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 ||
+      Hq % Hkv != 0 || check_mode(mode, k_win, pi, M, seg) != SA_OK)
+    return 0;
+  return bwd_layout(B, Hq, Hkv, N, d, has_skips(mode, k_win, pi, M, N)).total;
+}
+
+int sparse_attn_bwd(const void *q, const void *k, const void *v, const float *alpha, const void *o, const float *lse,
+                    const void *dO, void *dq, void *dk, void *dv, float *dalpha, int B, int Hq, int Hkv, int N, int d,
+                    int dtype, int mode, int k_win, int pi, int M, int seg, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  g_err[0] = 0;
+  int rc = check_shape(dtype, d);
+  if (rc != SA_OK) return rc;
+  if (dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "the backward pass supports bf16 I/O only");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and N must be >= 1");
+  if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
+  rc = check_mode(mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dO == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(SA_ERR_INVALID, "null tensor pointer");
+  const bool gated = mode == SA_MODE_PI && M > 0;
+  if (gated && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
+  if (mode == SA_MODE_PI && alpha != nullptr && dalpha == nullptr)
+    return fail(SA_ERR_INVALID, "dalpha is required when alpha is given (PI mode)");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(alpha, 4) ||
+      !aligned(dalpha, 4))
+    return fail(SA_ERR_INVALID, "misaligned tensor");
+  const long long rows = (long long)B * Hq * N;
+  if (rows >= (1LL << 31) || (long long)N * d >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
+  const bool skips = has_skips(mode, k_win, pi, M, N);
+  const BwdLayout L = bwd_layout(B, Hq, Hkv, N, d, skips);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_bwd_workspace_size()");
+  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t nq = (size_t)rows * d * 2, nkv = (size_t)B * Hkv * N * d * 2, nr = (size_t)rows * 4;
+  const void *ins[] = {q, k, v, o, dO, lse, alpha, workspace};
+  const size_t insz[] = {nq, nkv, nkv, nq, nq, nr, alpha ? nr : 0, L.total};
+  void *outs[] = {dq, dk, dv, dalpha};
+  const size_t outsz[] = {nq, nkv, nkv, dalpha ? nr : 0};
+  for (int a = 0; a < 4; ++a) {
+    for (int bb = 0; bb < 8; ++bb)
+      if (overlap(outs[a], outsz[a], ins[bb], insz[bb])) return fail(SA_ERR_INVALID, "a gradient overlaps an input or the workspace");
+    for (int bb = 0; bb < 4; ++bb)
+      if (bb != a && overlap(outs[a], outsz[a], outs[bb], outsz[bb])) return fail(SA_ERR_INVALID, "gradients overlap");
+  }
+  sa::BwdArgs ba;
+  ba.q = q; ba.k = k; ba.v = v; ba.o = o; ba.dO = dO; ba.alpha = mode == SA_MODE_PI ? alpha : nullptr; ba.lse = lse;
+  ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dalpha = mode == SA_MODE_PI && alpha != nullptr ? dalpha : nullptr;
+  char *w = (char *)workspace;
+  ba.Dv = (float *)(w + L.dv_off);
+  ba.cv = (float *)(w + L.cv_off);
+  ba.dq_s = skips ? (float *)(w + L.dqs_off) : nullptr;
+  ba.dk_s = skips ? (float *)(w + L.dks_off) : nullptr;
+  ba.dv_s = skips ? (float *)(w + L.dvs_off) : nullptr;
+  ba.B = B; ba.Hq = Hq; ba.Hkv = Hkv; ba.N = N; ba.d = d;
+  ba.mode = mode; ba.k_win = k_win; ba.pi = pi; ba.M = M; ba.seg = seg;
+  ba.m_min = skips ? (int)skip_m_min(k_win, pi) : 1;
+  hipError_t e = sa::launch_bwd(ba, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   return SA_OK;
 }

@@ -39,6 +39,7 @@ __device__ __forceinline__ u32x4 load_once16(const void *p) {
 // Running-max sentinel: finite, so exp2(sentinel - x) is 0 and sentinel - sentinel is 0.
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short u) {
   return __uint_as_float(((unsigned int)u) << 16);
@@ -84,5 +85,65 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   const int xcd = bid % 8, idx = bid / 8;
   return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
+
+// First key position of query i's window (window / pi-Attention: [i-k, i]) or
+// paired half-segments (ECP: [(floor(i/s)-1)*s, i]), clipped at 0.  Mode
+// numbers as in kernels.hpp (kModeEcp = 2).
+__device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
+  if (mode == 2) {
+    const int lo = (i / seg - 1) * seg;
+    return lo > 0 ? lo : 0;
+  }
+  const int lo = i - k_win;
+  return lo > 0 ? lo : 0;
+}
+
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Row-major bf16 tiles (64 rows) go from HBM straight into LDS
+// (global_load_lds_dwordx4: no staging registers), rows unpadded with the
+// 16-byte chunks of row r permuted by chunk ^ swz(r).  swz makes both LDS read
+// patterns conflict-free:
+//  * MFMA row-fragment reads (16 lanes = 16 consecutive rows, one chunk each)
+//    need swz to be a bijection on rows of equal bank offset;
+//  * transposed reads (32 lanes = 4 consecutive rows x 4 chunks) need the
+//    4 rows' 4-chunk groups to land on disjoint banks.
+// d = 64 (128-byte rows, two rows per bank sweep): swz(r) = (r1 << 2) | r3r2;
+// d = 128 (256-byte rows): swz(r) = (r1r0 << 2) | r3r2.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// One 16-byte direct-to-LDS load per lane: lane L's bytes land at
+// lds_base + 16 * L.  Issued through inline asm so that the compiler does not
+// wait for it before unrelated LDS reads; the caller waits (vmcnt) itself.
+__device__ __forceinline__ void dma16(const void *gbase, unsigned voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory");
+}
+
+// 4 bytes per lane to LDS address lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const void *gbase, unsigned voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace sa

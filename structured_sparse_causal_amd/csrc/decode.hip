@@ -39,14 +39,6 @@ struct Params {
   float scale_log2;
 };
 
-__device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
-  if (mode == kModeEcp) {
-    const int lo = (i / seg - 1) * seg;
-    return lo > 0 ? lo : 0;
-  }
-  const int lo = i - k_win;
-  return lo > 0 ? lo : 0;
-}
 
 // Rows of this split: count and position of row r.
 struct SplitRows {

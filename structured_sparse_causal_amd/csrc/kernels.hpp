@@ -20,6 +20,7 @@ struct PrefillArgs {
   void *o;
   const float *skip_ml; // [B*Hq*N][2] (running max in log2 units, sum) or nullptr
   const void *skip_acc; // [B*Hq*N][d] unnormalised skip accumulators (I/O dtype) or nullptr
+  float *lse;           // [B*Hq*N] natural-log row normaliser (training forward) or nullptr
   int B, Hq, Hkv, N, d, dtype;
   int mode, k_win, seg;
   int skip_first;       // first query position that has a skip key (PI), else N
@@ -45,7 +46,19 @@ struct DecodeArgs {
   int n_wsplit, chunk, nsplit;   // window splits, rows per window split, n_wsplit + 1
 };
 
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dO;   // bf16
+  const float *alpha, *lse;         // [B,Hq,N]
+  void *dq, *dk, *dv;               // bf16
+  float *dalpha;                    // [B,Hq,N] or nullptr
+  float *Dv, *cv;                   // workspace [B*Hq*N (+pad)]
+  float *dq_s, *dk_s, *dv_s; // workspace skip contributions, or nullptr
+  int B, Hq, Hkv, N, d;
+  int mode, k_win, pi, M, m_min, seg;
+};
+
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 hipError_t launch_skip(const SkipArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 

@@ -42,6 +42,7 @@ struct Params {
   void *o;
   const float *skip_ml;
   const void *skip_acc;
+  float *lse;             // [B*Hq*N] natural-log normaliser per row, or nullptr
   int N, Hq, Hkv, mode, k_win, seg, nqb, total, skip_first;
   int heads_per_xcd;   // > 0: heavy-first block order per XCD (see block_of)
   int rank_group;      // heads walked together in rank order (divides heads_per_xcd)
@@ -49,14 +50,6 @@ struct Params {
   float scale_log2;
 };
 
-__device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
-  if (mode == kModeEcp) {
-    const int lo = (i / seg - 1) * seg;
-    return lo > 0 ? lo : 0;
-  }
-  const int lo = i - k_win;
-  return lo > 0 ? lo : 0;
-}
 
 // Work order.  A query block's cost is its number of key tiles, which varies
 // with the block: ECP blocks in half-segment 0 and early in a half-segment are
@@ -105,15 +98,7 @@ __device__ __forceinline__ BlockId block_of(const Params &p, int bid) {
   return r;
 }
 
-__device__ __forceinline__ float half_swap_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 
-__device__ __forceinline__ float half_swap_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // fp32 I/O (small problems, exact-arithmetic checks): the same walk over key
 // tiles with v_mfma_f32_32x32x2f32, one LDS buffer (rows padded by 16 bytes)
@@ -248,6 +233,8 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
 
   const float l_tot = half_swap_sum(l_run);
   if (!qvalid) return;
+  // Row normaliser (natural log): scores are carried in log2 units.
+  if (p.lse != nullptr && h == 0) p.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot)) * kLn2;
   const float inv = 1.0f / l_tot;
   float *op = (float *)p.o + ((size_t)bh * N + qi) * D;
 #pragma unroll
@@ -261,34 +248,6 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 I/O.  K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4:
-// no staging registers), rows unpadded with the 16-byte chunks of row r
-// permuted by chunk ^ swz(r).  swz makes both LDS read patterns conflict-free:
-//  * K fragment reads (16 lanes = 16 consecutive rows, one chunk each) need
-//    swz to be a bijection on rows of equal bank offset;
-//  * transposed V reads (32 lanes = 4 consecutive rows x 4 chunks) need the
-//    4 rows' 4-chunk groups to land on disjoint banks.
-// d = 64 (128-byte rows, two rows per bank sweep): swz(r) = (r1 << 2) | r3r2;
-// d = 128 (256-byte rows): swz(r) = (r1r0 << 2) | r3r2.
-// ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int tile_swz(int r) {
-  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  else return ((r & 3) << 2) | ((r >> 2) & 3);
-}
-
-// One 16-byte direct-to-LDS load per lane: lane L's bytes land at
-// lds_base + 16 * L.  Issued through inline asm so that the compiler does not
-// wait for it before unrelated LDS reads; the caller waits (vmcnt) itself.
-__device__ __forceinline__ void dma16(const void *gbase, unsigned voff, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(lds_base)
-               : "memory");
-}
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
@@ -492,6 +451,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // ---- epilogue: O = acc / l ---------------------------------------------
   const float l_tot = half_swap_sum(l_run);
   if (!qvalid) return;
+  // Row normaliser (natural log): scores are carried in log2 units.
+  if (p.lse != nullptr && h == 0) p.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot)) * kLn2;
   const float inv = 1.0f / l_tot;
   bf16 *op = (bf16 *)p.o + ((size_t)bh * N + qi) * D;
 #pragma unroll
@@ -511,7 +472,7 @@ template <typename T, int D>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   Params p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.o = a.o;
-  p.skip_ml = a.skip_ml; p.skip_acc = a.skip_acc;
+  p.skip_ml = a.skip_ml; p.skip_acc = a.skip_acc; p.lse = a.lse;
   p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.mode = a.mode; p.k_win = a.k_win; p.seg = a.seg;
   p.nqb = (a.N + BM - 1) / BM;
   p.total = a.B * a.Hq * p.nqb;

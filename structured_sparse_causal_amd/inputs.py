@@ -110,3 +110,11 @@ def decode_inputs(w: Workload, device="cpu", seed: Optional[int] = None, chunk_r
     if w.mode == "pi":
         alpha = torch.sigmoid(_normal((w.B, w.Hq), gen, dev, None))
     return q, caches[0], caches[1], lens, alpha
+
+
+def grad_output(w: Workload, device="cpu", seed: Optional[int] = None):
+    """dO [B,Hq,N,d] ~ N(0, 1) in the workload's dtype, from its own generator
+    (seed + 7919) so the forward inputs keep their bits."""
+    dev = torch.device(device)
+    gen = _gen((w.seed if seed is None else seed) + 7919, dev)
+    return _normal((w.B, w.Hq, w.N, w.d), gen, dev, None).to(w.torch_dtype)

@@ -61,3 +61,34 @@ def assert_close(out, ref, dtype: str, what: str = ""):
     if bad:
         s = error_stats(out, ref)
         raise AssertionError("%s: %s (stats %s)" % (what, "; ".join(bad), s))
+
+
+# Gradients of the bf16 backward pass against the fp64 oracle.  The kernels
+# round P and dS to bf16 (unit roundoff 2^-9 = 2e-3) before the MFMA products
+# and take D_i = dO_i . o_i from the bf16 forward output, so each gradient
+# entry carries a relative error of a few 2^-9 on terms of mixed sign; the
+# gates are relative to the gradient's own scale (gradients have no natural
+# absolute scale): mean|diff| <= 1.5e-2 * mean|ref|, max|diff| <= 3e-2 * max|ref|.
+GRAD_MEAN_REL = 1.5e-2
+GRAD_MAX_REL = 3e-2
+
+
+def grad_failures(out, ref) -> list:
+    s = error_stats(out, ref)
+    bad = []
+    if not s["finite"]:
+        bad.append("non-finite gradient")
+    if s["mean_abs"] > GRAD_MEAN_REL * s["mean_ref"] + 1e-6:
+        bad.append("mean_rel %.3e > %.1e" % (s["mean_abs"] / max(s["mean_ref"], 1e-30), GRAD_MEAN_REL))
+    if s["max_abs"] > GRAD_MAX_REL * s["max_ref"] + 1e-6:
+        bad.append("max_rel %.3e > %.1e" % (s["max_abs"] / max(s["max_ref"], 1e-30), GRAD_MAX_REL))
+    return bad
+
+
+def assert_grad_close(out, ref, what: str = ""):
+    bad = grad_failures(out, ref)
+    s = error_stats(out, ref)
+    print("%s: max_abs %.3e (max_ref %.3e) mean_abs %.3e (mean_ref %.3e)" % (
+        what, s["max_abs"], s["max_ref"], s["mean_abs"], s["mean_ref"]), flush=True)
+    if bad:
+        raise AssertionError("%s: %s (stats %s)" % (what, "; ".join(bad), s))

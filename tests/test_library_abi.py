@@ -134,3 +134,70 @@ def test_python_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         binding.fwd(q, q, q, mode="window", k_win=2)
+
+
+def fwd_lse(lib, lse=WS, **kw):
+    p = dict(q=Q, k=K, v=V, a=A, o=O, B=1, Hq=2, Hkv=2, N=256, d=64, dtype=BF16, mode=WINDOW,
+             k_win=32, pi=64, M=3, seg=0)
+    p.update(kw)
+    return lib.sparse_attn_fwd_lse(p["q"], p["k"], p["v"], p["a"], p["o"], lse, p["B"], p["Hq"], p["Hkv"],
+                                   p["N"], p["d"], p["dtype"], p["mode"], p["k_win"], p["pi"], p["M"],
+                                   p["seg"], None, 0, None)
+
+
+def test_fwd_lse_rejects(lib):
+    assert fwd_lse(lib, lse=None) == INVALID
+    assert b"lse" in lib.sparse_attn_last_error()
+    assert fwd_lse(lib, lse=WS + 2) == INVALID                     # misaligned
+    assert fwd_lse(lib, lse=Q + 64) == INVALID                     # overlaps q
+    assert b"lse overlaps" in lib.sparse_attn_last_error()
+    assert fwd_lse(lib, d=96) == UNSUPPORTED
+
+
+DO, DQ, DK, DV, DA, LSE = (0x10000000 * (i + 1) for i in range(6))
+
+
+def bwd(lib, q=Q, k=K, v=V, a=A, o=O, lse=LSE, dO=DO, dq=DQ, dk=DK, dv=DV, da=DA, B=1, Hq=2, Hkv=2,
+        N=256, d=64, dtype=BF16, mode=PI, k_win=32, pi=64, M=3, seg=0, ws=None, wsb=0):
+    return lib.sparse_attn_bwd(q, k, v, a, o, lse, dO, dq, dk, dv, da, B, Hq, Hkv, N, d, dtype, mode,
+                               k_win, pi, M, seg, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(Hq=3), INVALID),
+    (dict(N=0), INVALID), (dict(mode=ECP, seg=0), INVALID), (dict(lse=None), INVALID),
+    (dict(dO=None), INVALID), (dict(dk=None), INVALID), (dict(a=None), INVALID),
+    (dict(da=None), INVALID), (dict(dq=DQ + 8), INVALID), (dict(lse=LSE + 1), INVALID),
+    (dict(), WORKSPACE), (dict(ws=WS, wsb=64), WORKSPACE), (dict(ws=WS + 16, wsb=1 << 30), INVALID),
+    (dict(dq=Q, ws=WS, wsb=1 << 30), INVALID), (dict(dk=DQ + 256, ws=WS, wsb=1 << 30), INVALID),
+    (dict(da=LSE, ws=WS, wsb=1 << 30), INVALID), (dict(dv=WS + 1024, ws=WS, wsb=1 << 30), INVALID),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+    assert lib.sparse_attn_last_error() != b""
+
+
+def test_bwd_dalpha_optional_without_gate(lib):
+    # Window and ECP take no alpha and give no dalpha: validation passes them
+    # and stops at the overlapping gradient.
+    assert bwd(lib, a=None, da=None, mode=WINDOW, dq=Q, ws=WS, wsb=1 << 30) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+    assert bwd(lib, a=None, da=None, mode=ECP, seg=64, dq=Q, ws=WS, wsb=1 << 30) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+
+
+def test_bwd_workspace_sizes(lib):
+    ws = lib.sparse_attn_bwd_workspace_size
+    r256 = lambda x: -(-x // 256) * 256
+    # Per query row D_i = dO_i . o_i and c_i (lse and log-gate term), each with a
+    # 16-float tail; with skip keys also fp32 skip partials of dq, dk, dv.
+    rows, kv = 2 * 16 * 4096, 2 * 16 * 4096
+    assert ws(2, 16, 16, 4096, 64, BF16, WINDOW, 256, 0, 0, 0) == 2 * r256((rows + 16) * 4)
+    assert ws(2, 16, 16, 4096, 64, BF16, PI, 256, 1024, 3, 0) == (
+        2 * r256((rows + 16) * 4) + r256(rows * 64 * 4) + 2 * r256(kv * 64 * 4))
+    assert ws(1, 8, 2, 1000, 128, BF16, PI, 60, 70, 8, 0) == (
+        2 * r256((8000 + 16) * 4) + r256(8000 * 128 * 4) + 2 * r256(2000 * 128 * 4))
+    assert ws(1, 2, 2, 256, 64, BF16, PI, 300, 64, 4, 0) == 2 * r256((512 + 16) * 4)   # skips inside window
+    assert ws(1, 2, 2, 256, 64, BF16, ECP, 0, 0, 0, 64) == 2 * r256((512 + 16) * 4)
+    assert ws(1, 2, 2, 256, 64, F32, WINDOW, 8, 0, 0, 0) == 0                        # bf16 only
+    assert ws(1, 2, 2, 256, 80, BF16, WINDOW, 8, 0, 0, 0) == 0
