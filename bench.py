@@ -8,8 +8,9 @@ inputs already resident in HBM.  ``value`` is useful TFLOP/s: 4*d FLOPs per
 attended (query, key) pair, nothing for masked or padded work.  The same JSON
 line carries the roofline of the dominant kernel (timed live with HIP events
 on the launch stream), the other workloads of the hot path (pi-Attention
-prefill, the looped window block, GQA decode) and the CPU oracle timed on a
-bounded sample of the headline workload.
+prefill, the looped window block, GQA decode), the backward pass of one layer
+call on the three prefill shapes, and the CPU oracle timed on a bounded sample
+of the headline workload.
 
 Only one GPU is used; ``--gpus N`` with N > 1 exits with a message.
 """
@@ -221,6 +222,41 @@ def run_decode_workload(torch, sa, w, reps, warmup):
     return res
 
 
+def run_bwd_workload(torch, sa, w, reps, warmup):
+    """Backward pass of one layer call (bf16): gradients of q, k, v (and
+    alpha) given dO, from the o and lse of a training forward run before the
+    timed region.  Useful FLOP = 10*d per attended pair: the five contractions
+    of the standard attention backward (recomputed scores, dP, dV, dK, dQ,
+    2*d each), i.e. 2.5 times the forward's useful FLOP."""
+    from structured_sparse_causal_amd.inputs import grad_output, prefill_inputs
+    dev = torch.device("cuda:0")
+    q, k, v, a = prefill_inputs(w, device=dev)
+    dO = grad_output(w, device=dev)
+    prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    o = sa.fwd(q, k, v, a, lse=lse, **prm)
+    nbytes = sa.bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, q.dtype, w.mode, w.k_win, w.pi,
+                                   w.M, w.seg)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def fn():
+        sa.bwd(q, k, v, a, o, lse, dO, workspace=ws, **prm)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t = event_times(torch, fn, reps)
+    flop = 10.0 * w.d * pairs_per_head(w) * w.B * w.Hq
+    ms = float(np.median(t))
+    tf = flop / (ms * 1e-3) / 1e12
+    res = {
+        "ms": ms, "ms_p10": float(np.percentile(t, 10)), "ms_p90": float(np.percentile(t, 90)),
+        "useful_tflops": tf, "pct_bf16_mfma_peak": 100.0 * tf / MFMA_BF16_PEAK_TFLOPS,
+        "useful_flop": flop, "layer_calls": 1,
+    }
+    del q, k, v, a, dO, lse, o, ws
+    return res
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle (fp64, OpenMP over query rows) on a bounded sample of the
     workload: whole (batch, head) slices, grown until about budget_s of CPU
@@ -280,6 +316,11 @@ def main():
     sa.load_library()
     dev = torch.device("cuda:0")
     if args.only is not None:
+        if args.only.startswith("bwd_"):
+            wx = WORKLOADS[args.only[4:]].replace(loops=1)
+            print(json.dumps({"workload": args.only, **run_bwd_workload(torch, sa, wx, args.steps, args.warmup)}),
+                  flush=True)
+            return
         wx = WORKLOADS[args.only]
         run = run_decode_workload if wx.decode else run_prefill_workload
         print(json.dumps({"workload": wx.name, **run(torch, sa, wx, args.steps, args.warmup)}), flush=True)
@@ -354,6 +395,13 @@ def main():
             else:
                 extras[name] = run_prefill_workload(torch, sa, wx, reps, 3)
             log("  %s" % json.dumps(extras[name]))
+            torch.cuda.empty_cache()
+        # Backward pass (training) of one layer call on the prefill shapes.
+        for name in ("ecp_bf16", "pi_bf16", "window_loop_bf16"):
+            wx = WORKLOADS[name].replace(loops=1)
+            log("bench: backward %s (one layer call)" % name)
+            extras["bwd_" + name] = run_bwd_workload(torch, sa, wx, 10 if wx.d == 128 else 30, 3)
+            log("  %s" % json.dumps(extras["bwd_" + name]))
             torch.cuda.empty_cache()
 
     cpu = None

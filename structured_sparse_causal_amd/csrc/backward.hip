@@ -378,8 +378,10 @@ __device__ __forceinline__ int last_query(int j, const Params &p) {
 }
 
 // ---- dk and dv: key-stationary walk over the query tiles -------------------------
+// d = 128 holds K, V (64 VGPRs) and the dK, dV accumulators (128) per lane:
+// one wave per SIMD, with the 512-entry register budget that allows.
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(Params p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p) {
   constexpr int RB = D * 2, TILE = BN * RB, NQF = D / 16, NDB = D / 32;
   // Q0 Q1 dO0 dO1 tiles, then per-query c and D (two buffers of 64 floats each)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * 256];
@@ -411,6 +413,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(Params p) {
   const int t_begin = k0;                       // the first query that can see key k0 is k0
   const int ntiles = (hi_q - t_begin) / BN + 1;
   const int wq_hi = last_query(kw_last, p);   // last query seeing this wave's keys
+  const int w_lq_first = last_query(min(j_w, N - 1), p);   // last query seeing all of them
+  const bool w_allvalid = j_w + 31 < N;
+  // Query iq sees key kj iff kj <= iq <= last_query(kj) (key_lo is
+  // non-decreasing in iq); an invalid key gets an empty range.
+  const int vis_lo = kvalid ? kj : -(1 << 30);
+  const unsigned vis_span = kvalid ? (unsigned)(last_query(kj, p) - kj) : 0u;
   const TileOffsets<D> off(lane);
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
   const float *cl = (const float *)(smem + 4 * TILE);       // [2][64] c, then [2][64] D
@@ -446,55 +454,54 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(Params p) {
         const char *QB = smem + buf * TILE;
         const char *OB = smem + (2 + buf) * TILE;
         const float *cq = cl + 64 * buf, *dq = cl + 128 + 64 * buf;
-        f32x16 s[2], dp[2];
+        // every (query, key) of the tile visible: no per-element mask
+        const bool full = w_allvalid && i0 >= kw_last && i0 + BN - 1 <= w_lq_first;
+        // The 64 queries in two halves of 32 (fewer live accumulators).
 #pragma unroll
         for (int qb2 = 0; qb2 < 2; ++qb2) {
-          s[qb2] = f32x16{};
-          dp[qb2] = f32x16{};
+          f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
           for (int kk = 0; kk < NQF; ++kk) {
             const bf16x8 qa = *(const bf16x8 *)(QB + 32 * qb2 * RB + off.row[kk]);
             const bf16x8 oa = *(const bf16x8 *)(OB + 32 * qb2 * RB + off.row[kk]);
-            s[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s[qb2], 0, 0, 0);
-            dp[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp[qb2], 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
           }
-        }
-        // element (query i0 + 32 qb2 + 8(jj/4) + 4h + jj%4, key kj)
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2)
+          // element jj: query i0 + 32 qb2 + 8(jj/4) + 4h + jj%4, key kj
 #pragma unroll
           for (int j4 = 0; j4 < 4; ++j4) {
-            const int ql = 32 * qb2 + 8 * j4 + 4 * h;        // tile-local query of element 0
+            const int ql = 32 * qb2 + 8 * j4 + 4 * h;        // tile-local query of element 4 j4
             const f32x4 cvv = *(const f32x4 *)(cq + ql);
             const f32x4 dvv = *(const f32x4 *)(dq + ql);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int jj = 4 * j4 + e, iq = i0 + ql + e;
-              float pr = fast_exp2(fmaf(s[qb2][jj], p.scale_log2, cvv[e]));
-              const bool vis = kvalid && iq < N && kj <= iq && key_lo(iq, p.mode, p.k_win, p.seg) <= kj;
-              if (!vis) pr = 0.f;
-              s[qb2][jj] = pr;
-              dp[qb2][jj] = pr * (dp[qb2][jj] - dvv[e]);
+              const int jj = 4 * j4 + e;
+              float pr = fast_exp2(fmaf(s[jj], p.scale_log2, cvv[e]));
+              if (!full && (unsigned)(i0 + ql + e - vis_lo) > vis_span) pr = 0.f;
+              s[jj] = pr;
+              dp[jj] = pr * (dp[jj] - dvv[e]);
             }
           }
-        // dV^T += dO^T P, dK^T += Q^T dS
+          // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          bf16x8 pb, sb;
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int kk = 2 * qb2 + k2;
+            bf16x8 pb, sb;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pb[e] = (bf16)s[kk >> 1][8 * (kk & 1) + e];
-            sb[e] = (bf16)dp[kk >> 1][8 * (kk & 1) + e];
-          }
+            for (int e = 0; e < 8; ++e) {
+              pb[e] = (bf16)s[8 * k2 + e];
+              sb[e] = (bf16)dp[8 * k2 + e];
+            }
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const char *ob = OB + 16 * kk * RB, *qbp = QB + 16 * kk * RB;
-            const short4v olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][0]));
-            const short4v ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][1]));
-            const short4v qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][0]));
-            const short4v qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][1]));
-            adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(olo, ohi), pb, adv[db], 0, 0, 0);
-            adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(qlo, qhi), sb, adk[db], 0, 0, 0);
+            for (int db = 0; db < NDB; ++db) {
+              const char *ob = OB + 16 * kk * RB, *qbp = QB + 16 * kk * RB;
+              const short4v olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][0]));
+              const short4v ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][1]));
+              const short4v qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][0]));
+              const short4v qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][1]));
+              adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(olo, ohi), pb, adv[db], 0, 0, 0);
+              adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(qlo, qhi), sb, adk[db], 0, 0, 0);
+            }
           }
         }
       }
