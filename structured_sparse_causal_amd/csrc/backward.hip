@@ -22,10 +22,10 @@
 //
 // Kernels (one call runs them in this order):
 //   bwd_prep_kernel   D_i and c_i = log2(prior of local keys) - lse_i*log2(e)
-//   skip_bwd_q_kernel / skip_bwd_kv_kernel   (pi-Attention with skip keys)
-//       the skip-key contributions to dq (query-owned; also writes dalpha)
-//       and dk, dv (key-owned), fp32, written to the workspace; VALU dot
-//       products over the <= M skip keys of each row
+//   skip_bwd_kv_kernel / skip_bwd_q_kernel   (pi-Attention with skip keys)
+//       the skip-key contributions to dk, dv (key-owned) and dq, dalpha
+//       (query-owned), fp32, written to the workspace; 16x16 MFMA tiles over
+//       the residue chains i mod pi (one kernel when every chain is one tile)
 //   bwd_dq_kernel     query-stationary over the window / ECP keys: the
 //       forward's tile walk with S^T = K Q^T and dP^T = V dO^T on the matrix
 //       cores, dS, then dQ^T += K^T dS^T (K^T fragments by transposed LDS
@@ -56,6 +56,9 @@ struct Params {
   float *dq_s, *dk_s, *dv_s;            // skip contributions (nullptr without skips)
   int B, Hq, Hkv, N, mode, k_win, pi, M, m_min, seg, grp;
   int nqb, nkb;
+  // skip-key residue chains: periods per residue, first position with a skip
+  // key (m_min * pi), query- and key-period tiles per residue, wave counts
+  int P, skip_first, nqt, nkt, nwork_q, nwork_kv;
   float scale_log2, scale;
 };
 
@@ -88,115 +91,244 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Params p, long long rows)
   }
 }
 
-// ---- skip keys, query-owned: dq's skip term and the gate gradient -------------
-// 8 lanes per query row, D/8 dims each.  Writes every row (zeros without skips).
-template <int D>
-__global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p, long long rows) {
-  constexpr int L = 8, C = D / L;
-  const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = tid / L;
-  const int part = (int)(tid % L);
-  const bool live = row < rows;
-  const long long r = live ? row : 0;
-  const int i = (int)(r % p.N);
-  const long long bh = r / p.N;
-  const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq), g = h / p.grp;
-  const bf16 *kb = p.k + (size_t)(b * p.Hkv + g) * p.N * D + part * C;
-  const bf16 *vb = p.v + (size_t)(b * p.Hkv + g) * p.N * D + part * C;
-  float qv[C], dov[C], dq[C];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    qv[c] = (float)p.q[r * D + part * C + c];
-    dov[c] = (float)p.dO[r * D + part * C + c];
-    dq[c] = 0.f;
-  }
-  const float lse = p.lse[r], Dd = p.Dv[r];
-  const float a = p.alpha != nullptr ? p.alpha[r] : 1.f;
-  float da = 0.f;
-  // Skip keys i - m*pi, m = m_min..M, >= 0 (the same number on all 8 lanes).
-  const int mmax = (i - p.m_min * p.pi) >= 0 ? min(p.M, i / p.pi) : p.m_min - 1;
-  for (int m = p.m_min; m <= mmax; ++m) {
-    const int j = i - m * p.pi;
-    float s = 0.f, dp = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      s = fmaf(qv[c], (float)kb[(size_t)j * D + c], s);
-      dp = fmaf(dov[c], (float)vb[(size_t)j * D + c], dp);
-    }
-#pragma unroll
-    for (int w = 1; w < L; w <<= 1) {
-      s += __shfl_xor(s, w, 64);
-      dp += __shfl_xor(dp, w, 64);
-    }
-    const float s0 = s * p.scale;                     // score without the prior
-    const float pnp = __expf(s0 - lse);               // P_ij / (1 - alpha_i)
-    const float ds = pnp * (1.0f - a) * (dp - Dd);    // dS_ij
-    da -= pnp * (dp - Dd);
-#pragma unroll
-    for (int c = 0; c < C; ++c) dq[c] = fmaf(ds * p.scale, (float)kb[(size_t)j * D + c], dq[c]);
-  }
-  if (!live) return;
-#pragma unroll
-  for (int c = 0; c < C; ++c) p.dq_s[r * D + part * C + c] = dq[c];
-  if (part == 0 && p.dalpha != nullptr) p.dalpha[r] = da / a;
+// ---- skip keys: residue chains -------------------------------------------------
+// Query i and its skip keys i - m*pi share the residue r = i mod pi; with
+// period p = (i - r)/pi, query period p attends key periods p - m for
+// m in [m_min, M] (a small dense band per residue, pi-Attention section 2
+// item 2).  The 16x16 MFMAs run on tiles of 16 periods of one residue:
+//   16x16x32 (K = dims): S = Q K^T and dP = dO V^T (rows queries, columns
+//     keys), or with swapped operands S^T, dP^T (rows keys, columns queries);
+//   16x16x16 (K = 16 periods): dV^T += dO^T P, dK^T += Q^T dS, dQ^T += K^T dS^T
+//     with the transposed operand read from a per-wave LDS copy of the rows
+//     the wave holds in registers.
+// Skip keys carry the prior log(1 - alpha_i): P = (1 - alpha_i) exp(s - lse_i).
+// The gate gradient's skip sum uses exp(s - lse_i) (dP - D_i) directly, so it
+// stays finite at alpha_i = 1.
+
+// Transposed 16x16 operand from a wave's LDS rows: lane (G, t) gets
+// rows 4G..4G+3 at column c0 + t.
+template <int LD>
+__device__ __forceinline__ bf16x4 lds_tr16(const bf16 *rows, int c0, int G, int t) {
+  const bf16 *src = rows + (4 * G + (t >> 2)) * LD + c0 + 4 * (t & 3);
+  return as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src));
 }
 
-// ---- skip keys, key-owned: dk and dv ------------------------------------------
-// 8 lanes per key row of [B, Hkv, N]; loops over the GQA group's heads and the
-// queries j + m*pi that have key j as a skip key.  Writes every key row.
-template <int D>
-__global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p, long long kvrows) {
-  constexpr int L = 8, C = D / L;
-  const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = tid / L;
-  const int part = (int)(tid % L);
-  const bool live = row < kvrows;
-  const long long r = live ? row : 0;
-  const int j = (int)(r % p.N);
-  const long long bg = r / p.N;
-  const int b = (int)(bg / p.Hkv), g = (int)(bg % p.Hkv);
-  float kv[C], vv[C], dk[C], dv[C];
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Key-stationary: one wave per (batch, KV head, residue, tile of 16 key
+// periods); loops over the GQA group's heads and the query-period tiles that
+// have these keys as skip keys; writes dk, dv skip partials (fp32, dk scaled).
+// WITH_Q (every residue chain is one tile: P - m_min <= 16): the single query
+// tile holds every query of the chain and every skip key of those queries is
+// in this key tile, so the wave also writes the dq skip partial and dalpha.
+template <int D, bool WITH_Q>
+__global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
+  constexpr int LD = D + 8, NK = D / 32, ND = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 lds[4][(WITH_Q ? 3 : 2) * 16 * LD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int work = blockIdx.x * 4 + wave;
+  if (work >= p.nwork_kv) return;  // no block-level barrier below: waves are independent
+  const int kt = work % p.nkt;
+  const int r = (work / p.nkt) % p.pi;
+  const int bg = work / (p.nkt * p.pi);
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const int N = p.N;
+  const int G = lane >> 4, t = lane & 15;
+  const int k0 = 16 * kt;
+  const long long ikl = (long long)r + (long long)(k0 + t) * p.pi;
+  const bool kvalid = ikl < N;
+  const int ik = kvalid ? (int)ikl : 0;
+  const bf16 *Kp = p.k + (size_t)bg * N * D, *Vp = p.v + (size_t)bg * N * D;
+  bf16 *qs = lds[wave], *os = qs + 16 * LD, *ks = os + 16 * LD;
+
+  bf16x8 kf[NK], vf[NK];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    kv[c] = (float)p.k[r * D + part * C + c];
-    vv[c] = (float)p.v[r * D + part * C + c];
-    dk[c] = 0.f;
-    dv[c] = 0.f;
+  for (int kk = 0; kk < NK; ++kk) {
+    kf[kk] = kvalid ? *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
+    vf[kk] = kvalid ? *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
+    if (WITH_Q) *(bf16x8 *)(ks + t * LD + 32 * kk + 8 * G) = kf[kk];
   }
+  f32x4 adk[ND], adv[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    adk[db] = f32x4{};
+    adv[db] = f32x4{};
+  }
+  const int q_lo = k0 + p.m_min;
+  const int q_hi = min(p.P - 1, k0 + 15 + p.M);
   for (int hh = 0; hh < p.grp; ++hh) {
-    const size_t qrow0 = ((size_t)b * p.Hq + g * p.grp + hh) * p.N;
-    for (int m = p.m_min; m <= p.M; ++m) {
-      const long long il = (long long)j + (long long)m * p.pi;
-      if (il >= p.N) break;
-      const size_t qr = qrow0 + (size_t)il;
-      const bf16 *qp = p.q + qr * D + part * C, *dop = p.dO + qr * D + part * C;
-      float s = 0.f, dp = 0.f;
+    const size_t bh = (size_t)b * p.Hq + g * p.grp + hh;
+    const bf16 *Qp = p.q + bh * N * D, *Op = p.dO + bh * N * D;
+    for (int q0 = q_lo; q0 <= q_hi; q0 += 16) {
+      const long long iql = (long long)r + (long long)(q0 + t) * p.pi;
+      const bool qvalid = iql < N;
+      const int iq = qvalid ? (int)iql : 0;
+      const size_t qrow = bh * N + iq;
+      bf16x8 qa[NK], oa[NK];
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        s = fmaf((float)qp[c], kv[c], s);
-        dp = fmaf((float)dop[c], vv[c], dp);
+      for (int kk = 0; kk < NK; ++kk) {
+        qa[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
+        oa[kk] = qvalid ? *(const bf16x8 *)(Op + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
       }
+      const float c0 = qvalid ? -p.lse[qrow] * kLog2e : 0.f;
+      const float Dq = qvalid ? p.Dv[qrow] : 0.f;
+      const float al = qvalid ? p.alpha[qrow] : 1.f;
+      f32x4 sc = f32x4{}, dp = f32x4{};
 #pragma unroll
-      for (int w = 1; w < L; w <<= 1) {
-        s += __shfl_xor(s, w, 64);
-        dp += __shfl_xor(dp, w, 64);
+      for (int kk = 0; kk < NK; ++kk) {
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kf[kk], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[kk], vf[kk], dp, 0, 0, 0);
       }
-      const float a = p.alpha != nullptr ? p.alpha[qr] : 1.f;
-      const float P = __expf(s * p.scale - p.lse[qr]) * (1.0f - a);
-      const float ds = P * (dp - p.Dv[qr]);
+      wave_lds_sync();  // the previous tile's transposed reads are done
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        dk[c] = fmaf(ds * p.scale, (float)qp[c], dk[c]);
-        dv[c] = fmaf(P, (float)dop[c], dv[c]);
+      for (int kk = 0; kk < NK; ++kk) {
+        *(bf16x8 *)(qs + t * LD + 32 * kk + 8 * G) = qa[kk];
+        *(bf16x8 *)(os + t * LD + 32 * kk + 8 * G) = oa[kk];
+      }
+      // element jj: query period q0 + 4G + jj (its scalars live in lane 4G + jj), key period k0 + t
+      bf16x4 pb, sb;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int src = 4 * G + jj;
+        const float c0j = __shfl(c0, src, 64), Dj = __shfl(Dq, src, 64), aj = __shfl(al, src, 64);
+        const int qv = __shfl((int)qvalid, src, 64);
+        const int m = q0 + src - (k0 + t);
+        const bool ok = kvalid && qv && m >= p.m_min && m <= p.M;
+        const float pr = ok ? fast_exp2(fmaf(sc[jj], p.scale_log2, c0j)) * (1.0f - aj) : 0.f;
+        pb[jj] = (bf16)pr;
+        sb[jj] = (bf16)(pr * (dp[jj] - Dj));
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        adv[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(os, 16 * db, G, t), pb, adv[db], 0, 0, 0);
+        adk[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(qs, 16 * db, G, t), sb, adk[db], 0, 0, 0);
+      }
+      if (WITH_Q) {
+        // element jj: key period k0 + 4G + jj, query period q0 + t (this lane's query)
+        f32x4 st = f32x4{}, dpt = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qa[kk], st, 0, 0, 0);
+          dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kk], oa[kk], dpt, 0, 0, 0);
+        }
+        bf16x4 dsb;
+        float da = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int m = q0 + t - (k0 + 4 * G + jj);
+          const bool ok = qvalid && m >= p.m_min && m <= p.M;
+          const float pnp = ok ? fast_exp2(fmaf(st[jj], p.scale_log2, c0)) : 0.f;  // P / (1 - alpha)
+          const float d = dpt[jj] - Dq;
+          dsb[jj] = (bf16)(pnp * (1.0f - al) * d);
+          da -= pnp * d;
+        }
+        da += wave_shfl_xor(da, 16);
+        da += wave_shfl_xor(da, 32);
+        f32x4 aq[ND];
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          aq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(ks, 16 * db, G, t), dsb, f32x4{}, 0, 0, 0);
+        if (qvalid) {
+          float *dst = p.dq_s + qrow * D;
+#pragma unroll
+          for (int db = 0; db < ND; ++db) *(f32x4 *)(dst + 16 * db + 4 * G) = aq[db] * p.scale;
+          if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
+        }
       }
     }
   }
-  if (!live) return;
+  if (!kvalid) return;
+  const size_t krow = (size_t)bg * N + ik;
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    p.dk_s[r * D + part * C + c] = dk[c];
-    p.dv_s[r * D + part * C + c] = dv[c];
+  for (int db = 0; db < ND; ++db) {
+    *(f32x4 *)(p.dk_s + krow * D + 16 * db + 4 * G) = adk[db] * p.scale;
+    *(f32x4 *)(p.dv_s + krow * D + 16 * db + 4 * G) = adv[db];
   }
+}
+
+// Query-stationary (residue chains longer than one tile): one wave per
+// (batch, head, residue, tile of 16 query periods); loops over the key-period
+// tiles of their skip keys; writes the dq skip partial (fp32, scaled) and dalpha.
+template <int D>
+__global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
+  constexpr int LD = D + 8, NK = D / 32, ND = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 lds[4][16 * LD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int work = blockIdx.x * 4 + wave;
+  if (work >= p.nwork_q) return;  // no block-level barrier below
+  const int tile = work % p.nqt;
+  const int r = (work / p.nqt) % p.pi;
+  const size_t bh = (size_t)(work / (p.nqt * p.pi));
+  const int hq = (int)(bh % p.Hq), b = (int)(bh / p.Hq), g = hq / p.grp;
+  const int N = p.N;
+  const int G = lane >> 4, t = lane & 15;
+  const int p0 = p.m_min + 16 * tile;
+  const long long iql = (long long)r + (long long)(p0 + t) * p.pi;
+  const bool qvalid = iql < N;
+  const int iq = qvalid ? (int)iql : 0;
+  const size_t qrow = bh * N + iq;
+  const bf16 *Kp = p.k + (size_t)(b * p.Hkv + g) * N * D, *Vp = p.v + (size_t)(b * p.Hkv + g) * N * D;
+  bf16 *ks = lds[wave];
+  bf16x8 qa[NK], oa[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    qa[kk] = qvalid ? *(const bf16x8 *)(p.q + qrow * D + 32 * kk + 8 * G) : bf16x8{};
+    oa[kk] = qvalid ? *(const bf16x8 *)(p.dO + qrow * D + 32 * kk + 8 * G) : bf16x8{};
+  }
+  const float c0 = qvalid ? -p.lse[qrow] * kLog2e : 0.f;
+  const float Dq = qvalid ? p.Dv[qrow] : 0.f;
+  const float al = qvalid ? p.alpha[qrow] : 1.f;
+  f32x4 aq[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) aq[db] = f32x4{};
+  float da = 0.f;
+  const int kt_lo = max(0, p0 - p.M), kt_hi = p0 + 15 - p.m_min;
+  for (int kt = kt_lo; kt <= kt_hi; kt += 16) {
+    const long long ikl = (long long)r + (long long)(kt + t) * p.pi;
+    const bool kvalid = ikl < N;
+    const int ik = kvalid ? (int)ikl : 0;
+    bf16x8 ka[NK], va[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      ka[kk] = kvalid ? *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
+      va[kk] = kvalid ? *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
+    }
+    // element jj: key period kt + 4G + jj, query period p0 + t
+    f32x4 st = f32x4{}, dpt = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qa[kk], st, 0, 0, 0);
+      dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kk], oa[kk], dpt, 0, 0, 0);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) *(bf16x8 *)(ks + t * LD + 32 * kk + 8 * G) = ka[kk];
+    bf16x4 dsb;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int m = p0 + t - (kt + 4 * G + jj);
+      const bool ok = qvalid && m >= p.m_min && m <= p.M;
+      const float pnp = ok ? fast_exp2(fmaf(st[jj], p.scale_log2, c0)) : 0.f;
+      const float d = dpt[jj] - Dq;
+      dsb[jj] = (bf16)(pnp * (1.0f - al) * d);
+      da -= pnp * d;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      aq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(ks, 16 * db, G, t), dsb, aq[db], 0, 0, 0);
+  }
+  da += wave_shfl_xor(da, 16);
+  da += wave_shfl_xor(da, 32);
+  if (!qvalid) return;
+#pragma unroll
+  for (int db = 0; db < ND; ++db) *(f32x4 *)(p.dq_s + qrow * D + 16 * db + 4 * G) = aq[db] * p.scale;
+  if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
 }
 
 // Store 16 accumulator values of a 32x32 C tile (rows 8(j/4) + 4h + j%4 of the
@@ -367,8 +499,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
     __syncthreads();
   }
   if (!qvalid) return;
-  store_rows_bf16<D>(p.dq + row * D, acc, p.scale, p.dq_s != nullptr ? p.dq_s + row * D : nullptr, h);
-  if (p.dalpha != nullptr && p.dq_s == nullptr && h == 0) p.dalpha[row] = 0.f;
+  // rows below m_min * pi have no skip key: no seed, and a zero gate gradient
+  const bool seeded = p.dq_s != nullptr && qi >= p.skip_first;
+  store_rows_bf16<D>(p.dq + row * D, acc, p.scale, seeded ? p.dq_s + row * D : nullptr, h);
+  if (p.dalpha != nullptr && !seeded && h == 0) p.dalpha[row] = 0.f;
 }
 
 // Last query position that has key j in its window / ECP range (at most N - 1).
@@ -510,8 +644,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
     }
   }
   if (!kvalid) return;
-  store_rows_bf16<D>(p.dk + krow * D, adk, p.scale, p.dk_s != nullptr ? p.dk_s + krow * D : nullptr, h);
-  store_rows_bf16<D>(p.dv + krow * D, adv, 1.0f, p.dv_s != nullptr ? p.dv_s + krow * D : nullptr, h);
+  // keys at or above N - m_min * pi are no query's skip key: no seed
+  const bool seeded = p.dk_s != nullptr && kj < N - p.skip_first;
+  store_rows_bf16<D>(p.dk + krow * D, adk, p.scale, seeded ? p.dk_s + krow * D : nullptr, h);
+  store_rows_bf16<D>(p.dv + krow * D, adv, 1.0f, seeded ? p.dv_s + krow * D : nullptr, h);
 }
 
 template <int D>
@@ -527,12 +663,25 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
   p.nkb = (a.N + BM - 1) / BM;
   p.scale = 1.0f / sqrtf((float)D);
   p.scale_log2 = kLog2e * p.scale;
-  const long long rows = (long long)a.B * a.Hq * a.N, kvrows = (long long)a.B * a.Hkv * a.N;
+  const long long rows = (long long)a.B * a.Hq * a.N;
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
+  p.P = (a.N + a.pi - 1) / (a.pi > 0 ? a.pi : 1);
+  p.skip_first = 0;
+  p.nqt = p.nkt = p.nwork_q = p.nwork_kv = 0;
   if (p.dq_s != nullptr) {
-    hipLaunchKernelGGL((skip_bwd_q_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
-    hipLaunchKernelGGL((skip_bwd_kv_kernel<D>), dim3((unsigned)((kvrows * 8 + 255) / 256)), dim3(256), 0, s, p,
-                       kvrows);
+    // skips exist, so m_min * pi < N
+    p.skip_first = a.m_min * a.pi;
+    p.nqt = p.nkt = (p.P - a.m_min + 15) / 16;
+    const long long wq = (long long)a.B * a.Hq * a.pi * p.nqt;
+    if (wq > (1LL << 30)) return hipErrorInvalidValue;   // wave count beyond the 1-D grid
+    p.nwork_q = (int)wq;
+    p.nwork_kv = (int)((long long)a.B * a.Hkv * a.pi * p.nkt);
+    if (p.nqt == 1) {
+      hipLaunchKernelGGL((skip_bwd_kv_kernel<D, true>), dim3((p.nwork_kv + 3) / 4), dim3(256), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((skip_bwd_kv_kernel<D, false>), dim3((p.nwork_kv + 3) / 4), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((skip_bwd_q_kernel<D>), dim3((p.nwork_q + 3) / 4), dim3(256), 0, s, p);
+    }
   }
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.Hq * p.nqb), dim3(256), 0, s, p);
   hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);

@@ -46,6 +46,9 @@ BWD_CASES = [
     Workload("bwd_pi_pi1", "pi", "bf16", 1, 1, 1, 300, 64, k_win=5, pi=1, M=20, seed=64),
     Workload("bwd_pi_noskip", "pi", "bf16", 2, 2, 2, 300, 64, k_win=70, pi=50, M=0, seed=65),
     Workload("bwd_pi_many_periods", "pi", "bf16", 1, 2, 1, 2100, 64, k_win=40, pi=48, M=30, seed=66),
+    # residue chains longer than one 16-period tile, with GQA and d = 128
+    Workload("bwd_pi_gqa_long", "pi", "bf16", 1, 4, 2, 1500, 64, k_win=20, pi=16, M=12, seed=69),
+    Workload("bwd_pi_long_d128", "pi", "bf16", 1, 2, 1, 900, 128, k_win=30, pi=20, M=9, seed=70),
     Workload("bwd_window_d128", "window", "bf16", 1, 2, 2, 1000, 128, k_win=300, seed=71),
     Workload("bwd_window_gqa", "window", "bf16", 2, 4, 2, 640, 64, k_win=129, seed=72),
     Workload("bwd_window_dense", "window", "bf16", 1, 2, 2, 333, 64, k_win=5000, seed=73),
