@@ -15,7 +15,7 @@ import torch
 import oracle
 import structured_sparse_causal_amd as sa
 from parity import assert_close, assert_grad_close
-from structured_sparse_causal_amd.inputs import Workload, grad_output, prefill_inputs
+from structured_sparse_causal_amd.inputs import WORKLOADS, Workload, grad_output, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -140,3 +140,58 @@ def test_bwd_gqa_equals_repeated_heads():
     assert_grad_close(da.cpu().numpy(), ma.cpu().numpy(), "gqa dalpha")
     assert_grad_close(dk.float().cpu().numpy(), mk.float().sum(1, keepdim=True).cpu().numpy(), "gqa dk")
     assert_grad_close(dv.float().cpu().numpy(), mv.float().sum(1, keepdim=True).cpu().numpy(), "gqa dv")
+
+
+# ---- full-size workloads, in the launch configuration the benchmark times ----
+
+def gpu_full_train_step(w: Workload):
+    q, k, v, a = prefill_inputs(w, device=DEV)
+    dO = grad_output(w, device=DEV)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=DEV)
+    o = sa.fwd(q, k, v, a, lse=lse, **prm(w))
+    grads = sa.bwd(q, k, v, a, o, lse, dO, **prm(w))
+    torch.cuda.synchronize()
+    return (q, k, v, a, dO), lse, grads
+
+
+@pytest.mark.parametrize("name,heads", [("ecp_bf16", [(0, 0), (3, 11)]),
+                                        ("pi_bf16", [(0, 0), (1, 15)])])
+def test_bwd_full_size_head_slices(name, heads):
+    # Hq = Hkv for these workloads, so one (batch, head) slice is a closed
+    # problem: the oracle computes its gradients exactly.
+    w = WORKLOADS[name]
+    say("full-size backward %s" % name)
+    (q, k, v, a, dO), lse, (dq, dk, dv, da) = gpu_full_train_step(w)
+    for b, h in heads:
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        a_sl = sl(a) if w.mode == "pi" else None
+        ref_lse = oracle.lse(sl(q), sl(k), a_sl, **prm(w))
+        assert np.abs(sl(lse).numpy() - ref_lse).max() <= 2e-3 * max(1.0, np.abs(ref_lse).max())
+        rq, rk, rv, ra = oracle.bwd(sl(q), sl(k), sl(v), a_sl, sl(dO), **prm(w))
+        tag = "%s b%d h%d" % (name, b, h)
+        assert_grad_close(sl(dq).float().numpy(), rq, tag + " dq")
+        assert_grad_close(sl(dk).float().numpy(), rk, tag + " dk")
+        assert_grad_close(sl(dv).float().numpy(), rv, tag + " dv")
+        if w.mode == "pi":
+            assert_grad_close(sl(da).numpy(), ra, tag + " dalpha")
+
+
+def test_bwd_full_size_window_subsequences():
+    # Window mode is local: dq of rows [s0, s0+R) and dk, dv of keys [s0, s0+R)
+    # depend only on positions [s0 - k, s0 + R + k) (every query that sees those
+    # keys has its whole window there), so the oracle on that sub-sequence gives
+    # their exact values.
+    w = WORKLOADS["window_loop_bf16"].replace(loops=1)
+    say("full-size backward %s (one layer call)" % w.name)
+    (q, k, v, _, dO), _, (dq, dk, dv, _) = gpu_full_train_step(w)
+    K, R = w.k_win, 384
+    for h, s0 in ((0, 0), (17, 30001), (31, w.N - R)):
+        lo, hi = max(0, s0 - K), min(w.N, s0 + R + K)
+        sub = lambda t: t[:, h:h + 1, lo:hi].cpu()
+        rq, rk, rv, _ = oracle.bwd(sub(q), sub(k), sub(v), None, sub(dO), mode="window", k_win=K)
+        r0 = s0 - lo
+        tag = "window h%d rows %d.." % (h, s0)
+        got = lambda t: t[:, h:h + 1, s0:s0 + R].float().cpu().numpy()
+        assert_grad_close(got(dq), rq[:, :, r0:r0 + R], tag + " dq")
+        assert_grad_close(got(dk), rk[:, :, r0:r0 + R], tag + " dk")
+        assert_grad_close(got(dv), rv[:, :, r0:r0 + R], tag + " dv")
