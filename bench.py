@@ -222,6 +222,59 @@ def run_decode_workload(torch, sa, w, reps, warmup):
     return res
 
 
+def run_decode_layouts(torch, sa, w, reps, warmup):
+    """The decode workload over serving-cache layouts holding the same rows:
+    paged pools (page size 16 and 64, pages at seeded random physical slots)
+    and a ring of max(k_win, M*pi) + 1 rows.  Same algorithmic bytes as the
+    contiguous decode; the paged call also reads its block-table entries."""
+    from structured_sparse_causal_amd.inputs import decode_inputs
+    dev = torch.device("cuda:0")
+    q, kc, vc, lens, a = decode_inputs(w, device=dev)
+    _, nb = decode_useful(w)
+    prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+    out = torch.empty_like(q)
+    res = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = event_times(torch, fn, reps)
+        ms = float(np.median(t))
+        return {"ms": ms, "useful_GBps": nb / (ms * 1e-3) / 1e9,
+                "pct_hbm_peak": 100.0 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "tokens_per_s": w.B / (ms * 1e-3)}
+
+    B, H, L, d = kc.shape
+    for P in (16, 64):
+        npg = L // P
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(1000 + P)
+        perm = torch.randperm(B * npg, generator=gen).to(dev)
+        pools = []
+        for c in (kc, vc):
+            pool = torch.empty((B * npg, H, P, d), dtype=c.dtype, device=dev)
+            pool[perm] = c.view(B, H, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, H, P, d)
+            pools.append(pool)
+        table = perm.view(B, npg).to(torch.int32).contiguous()
+        nbytes = sa.binding.load_library().sparse_attn_decode_paged_workspace_size(
+            B, w.Hq, H, P, npg, d, 1, sa.binding._mode(w.mode), w.k_win, w.pi, w.M, w.seg)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        res["paged_p%d" % P] = timed(lambda: sa.decode_paged(q, pools[0], pools[1], table, lens, a, out=out,
+                                                            workspace=ws, **prm))
+        del pools, table, ws
+        torch.cuda.empty_cache()
+    R = max(w.k_win, w.M * w.pi if w.mode == "pi" else 0) + 1
+    pos = torch.arange(L - R, L, device=dev)
+    rings = []
+    for c in (kc, vc):
+        r = torch.empty((B, H, R, d), dtype=c.dtype, device=dev)
+        r[:, :, pos % R] = c[:, :, pos]
+        rings.append(r)
+    res["ring_R%d" % R] = timed(lambda: sa.decode_ring(q, rings[0], rings[1], lens, a, out=out, **prm))
+    del q, kc, vc, lens, a, rings, out
+    return res
+
+
 def run_bwd_workload(torch, sa, w, reps, warmup):
     """Backward pass of one layer call (bf16): gradients of q, k, v (and
     alpha) given dO, from the o and lse of a training forward run before the
@@ -316,6 +369,11 @@ def main():
     sa.load_library()
     dev = torch.device("cuda:0")
     if args.only is not None:
+        if args.only == "decode_layouts":
+            print(json.dumps({"workload": args.only,
+                              **run_decode_layouts(torch, sa, WORKLOADS["decode_pi_gqa_bf16"], args.steps,
+                                                   args.warmup)}), flush=True)
+            return
         if args.only.startswith("bwd_"):
             wx = WORKLOADS[args.only[4:]].replace(loops=1)
             print(json.dumps({"workload": args.only, **run_bwd_workload(torch, sa, wx, args.steps, args.warmup)}),
@@ -396,6 +454,19 @@ def main():
                 extras[name] = run_prefill_workload(torch, sa, wx, reps, 3)
             log("  %s" % json.dumps(extras[name]))
             torch.cuda.empty_cache()
+        # Serving decode: cache layouts, and throughput over cache lengths.
+        wd = WORKLOADS["decode_pi_gqa_bf16"]
+        log("bench: decode over paged and ring caches")
+        extras["decode_layouts"] = run_decode_layouts(torch, sa, wd, 20, 3)
+        log("  %s" % json.dumps(extras["decode_layouts"]))
+        torch.cuda.empty_cache()
+        flat = {}
+        for L in (4096, 8192, 16384, 32768):
+            r = run_decode_workload(torch, sa, wd.replace(N=L), 20, 3)
+            flat[str(L)] = {k: r[k] for k in ("ms", "tokens_per_s", "useful_GBps", "useful_bytes")}
+            torch.cuda.empty_cache()
+        extras["decode_cache_length_sweep"] = flat
+        log("  decode over cache lengths: %s" % json.dumps(flat))
         # Backward pass (training) of one layer call on the prefill shapes.
         for name in ("ecp_bf16", "pi_bf16", "window_loop_bf16"):
             wx = WORKLOADS[name].replace(loops=1)

@@ -175,6 +175,46 @@ int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                        int mode, int k_win, int pi, int M, int seg,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Serving-cache layouts for the same decode (bf16 I/O only; fp32 returns
+ * SA_ERR_UNSUPPORTED).  Semantics, q, alpha, o, cache_lens and workspace as
+ * sparse_attn_decode; only where a position's key/value row lives differs.
+ *
+ * Ring cache: k_ring, v_ring [B, Hkv, R, d]; position p of sequence b lives in
+ * slot p mod R, so a stream of any length keeps only its last R tokens.  The
+ * keys of the query at position len - 1 must all still be resident: R must be
+ * at least the key span, k_win + 1 and (PI with M > 0) M*pi + 1, or 2*seg for
+ * ECP (else SA_ERR_INVALID).  cache_lens[b] >= 1 counts the tokens written so
+ * far (no upper bound); a length < 1 gives NaN outputs.
+ */
+size_t sparse_attn_decode_ring_workspace_size(int B, int Hq, int Hkv, int R, int d, int dtype,
+                                              int mode, int k_win, int pi, int M, int seg);
+int sparse_attn_decode_ring(const void *q, const void *k_ring, const void *v_ring,
+                            const int *cache_lens, const float *alpha, void *o,
+                            int B, int Hq, int Hkv, int R, int d, int dtype,
+                            int mode, int k_win, int pi, int M, int seg,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Paged cache: a pool of num_pages pages, k_pages, v_pages
+ * [num_pages, Hkv, page_size, d] (a page holds page_size consecutive positions
+ * of one sequence for every KV head), and block_table int32 [B, max_pages] in
+ * DEVICE memory: logical page j = p / page_size of sequence b is physical page
+ * block_table[b, j].  page_size is a power of two in [8, 4096]; PI mode takes
+ * M <= 63 (else SA_ERR_UNSUPPORTED).  cache_lens[b] must lie in
+ * [1, max_pages * page_size]; a length outside that range, or a table entry
+ * the query needs that lies outside [0, num_pages), gives NaN outputs for that
+ * sequence and reads no cache row.
+ */
+size_t sparse_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int max_pages,
+                                               int d, int dtype, int mode, int k_win, int pi, int M,
+                                               int seg);
+int sparse_attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                             const int *block_table, const int *cache_lens, const float *alpha,
+                             void *o, int B, int Hq, int Hkv, int num_pages, int page_size,
+                             int max_pages, int d, int dtype, int mode, int k_win, int pi, int M,
+                             int seg, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *sparse_attn_status_string(int status);
 

@@ -32,6 +32,8 @@ _lib = None
 EXPORTED = ("sparse_attn_fwd_workspace_size", "sparse_attn_fwd", "sparse_attn_fwd_lse",
             "sparse_attn_bwd_workspace_size", "sparse_attn_bwd",
             "sparse_attn_decode_workspace_size", "sparse_attn_decode",
+            "sparse_attn_decode_ring_workspace_size", "sparse_attn_decode_ring",
+            "sparse_attn_decode_paged_workspace_size", "sparse_attn_decode_paged",
             "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_version")
 
 
@@ -64,6 +66,14 @@ def load_library():
         lib.sparse_attn_bwd_workspace_size.argtypes = [i] * 11
         lib.sparse_attn_bwd.restype = i
         lib.sparse_attn_bwd.argtypes = [vp] * 11 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_decode_ring_workspace_size.restype = sz
+        lib.sparse_attn_decode_ring_workspace_size.argtypes = [i] * 11
+        lib.sparse_attn_decode_ring.restype = i
+        lib.sparse_attn_decode_ring.argtypes = [vp] * 6 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_decode_paged_workspace_size.restype = sz
+        lib.sparse_attn_decode_paged_workspace_size.argtypes = [i] * 12
+        lib.sparse_attn_decode_paged.restype = i
+        lib.sparse_attn_decode_paged.argtypes = [vp] * 7 + [i] * 13 + [vp, sz, vp]
         lib.sparse_attn_decode_workspace_size.restype = sz
         lib.sparse_attn_decode_workspace_size.argtypes = [i] * 11
         lib.sparse_attn_decode.restype = i
@@ -262,3 +272,60 @@ def loop_fwd(q, k, v, alpha=None, *, steps: int, mode, k_win: int = 0, pi: int =
                 out=outs[t % 2], workspace=workspace)
         vin = o
     return o
+
+
+def decode_ring(q, k_ring, v_ring, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
+                M: int = 0, seg: int = 0, out=None, workspace=None):
+    """Decode over ring caches [B,Hkv,R,d] (position p in slot p mod R); bf16.
+    cache_lens [B] int32 on the GPU counts the tokens written (query at len-1)."""
+    lib = load_library()
+    _need_gpu(q, k_ring, v_ring, cache_lens, alpha, out, workspace)
+    if q.dim() != 3 or k_ring.dim() != 4 or v_ring.shape != k_ring.shape:
+        raise ValueError("q must be [B, Hq, d] and rings [B, Hkv, R, d]")
+    if q.dtype != torch.bfloat16 or k_ring.dtype != q.dtype or v_ring.dtype != q.dtype:
+        raise NotImplementedError("ring caches take bf16 q and caches")
+    B, Hq, d = q.shape
+    Hkv, R = k_ring.shape[1], k_ring.shape[2]
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    m = _mode(mode)
+    out = torch.empty_like(q) if out is None else out
+    nbytes = int(lib.sparse_attn_decode_ring_workspace_size(B, Hq, Hkv, R, d, DTYPE_BF16, m, k_win, pi, M, seg))
+    ws = _workspace(max(nbytes, 256), q.device, workspace)
+    rc = lib.sparse_attn_decode_ring(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(cache_lens), _ptr(alpha), _ptr(out),
+                                     B, Hq, Hkv, R, d, DTYPE_BF16, m, int(k_win), int(pi), int(M), int(seg),
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device))
+    if rc != SA_OK:
+        _raise(lib, rc, "sparse_attn_decode_ring")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, cache_lens, alpha=None, *, mode, k_win: int = 0,
+                 pi: int = 0, M: int = 0, seg: int = 0, out=None, workspace=None):
+    """Decode over paged caches: pools [num_pages,Hkv,page_size,d], block_table
+    [B,max_pages] int32 (physical page of each logical page); bf16."""
+    lib = load_library()
+    _need_gpu(q, k_pages, v_pages, block_table, cache_lens, alpha, out, workspace)
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape or block_table.dim() != 2:
+        raise ValueError("q [B, Hq, d], pages [num_pages, Hkv, page_size, d], block_table [B, max_pages]")
+    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise NotImplementedError("paged caches take bf16 q and caches")
+    B, Hq, d = q.shape
+    num_pages, Hkv, P = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if block_table.dtype != torch.int32 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    max_pages = block_table.shape[1]
+    m = _mode(mode)
+    out = torch.empty_like(q) if out is None else out
+    nbytes = int(lib.sparse_attn_decode_paged_workspace_size(B, Hq, Hkv, P, max_pages, d, DTYPE_BF16, m, k_win,
+                                                              pi, M, seg))
+    ws = _workspace(max(nbytes, 256), q.device, workspace)
+    rc = lib.sparse_attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(cache_lens),
+                                      _ptr(alpha), _ptr(out), B, Hq, Hkv, num_pages, P, max_pages, d, DTYPE_BF16, m,
+                                      int(k_win), int(pi), int(M), int(seg), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(q.device))
+    if rc != SA_OK:
+        _raise(lib, rc, "sparse_attn_decode_paged")
+    return out

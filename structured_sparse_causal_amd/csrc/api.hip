@@ -272,44 +272,138 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d
   return round_up((size_t)B * Hq * (nw + 1) * (d + 4) * sizeof(float), 256);
 }
 
+namespace {
+
+// Shared body of the three decode entry points.  Lplan: the largest position
+// count the layout can hold (contiguous Lmax, ring R, paged max_pages * P);
+// cache_bytes: bytes of each cache tensor (overlap checks).
+int decode_impl(const void *q, const void *k_cache, const void *v_cache, const int *table, const int *cache_lens,
+                const float *alpha, void *o, int B, int Hq, int Hkv, int Lplan, int d, int dtype, int mode, int k_win,
+                int pi, int M, int seg, int layout, int R, int page_shift, int num_pages, int max_pages,
+                size_t cache_bytes, void *workspace, size_t workspace_bytes, void *stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || o == nullptr)
+    return fail(SA_ERR_INVALID, "null tensor pointer");
+  if (layout == sa::kCachePaged && table == nullptr) return fail(SA_ERR_INVALID, "null block table");
+  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(alpha, 4) || !aligned(cache_lens, 4) || !aligned(table, 4))
+    return fail(SA_ERR_INVALID, "misaligned tensor");
+  if ((long long)Lplan * d >= (1LL << 31) || B > 65535) return fail(SA_ERR_INVALID, "problem too large");
+  const size_t need = sparse_attn_decode_workspace_size(B, Hq, Hkv, Lplan, d, dtype, mode, k_win, pi, M, seg);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the decode workspace size");
+  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * d * es;
+  const size_t ntab = layout == sa::kCachePaged ? (size_t)B * max_pages * 4 : 0;
+  if (overlap(o, nq, q, nq) || overlap(o, nq, k_cache, cache_bytes) || overlap(o, nq, v_cache, cache_bytes) ||
+      overlap(o, nq, alpha, alpha ? (size_t)B * Hq * 4 : 0) || overlap(o, nq, cache_lens, (size_t)B * 4) ||
+      overlap(o, nq, table, ntab) || overlap(o, nq, workspace, need) ||
+      overlap(workspace, need, q, nq) || overlap(workspace, need, k_cache, cache_bytes) ||
+      overlap(workspace, need, v_cache, cache_bytes) || overlap(workspace, need, cache_lens, (size_t)B * 4) ||
+      overlap(workspace, need, table, ntab) || overlap(workspace, need, alpha, alpha ? (size_t)B * Hq * 4 : 0))
+    return fail(SA_ERR_INVALID, "output or workspace overlaps another tensor");
+  sa::DecodeArgs da;
+  da.q = q; da.kc = k_cache; da.vc = v_cache; da.lens = cache_lens; da.alpha = alpha; da.o = o;
+  da.ws = (float *)workspace;
+  da.B = B; da.Hq = Hq; da.Hkv = Hkv; da.Lmax = Lplan; da.d = d; da.dtype = dtype;
+  da.mode = mode; da.k_win = k_win; da.pi = pi; da.M = M; da.seg = seg;
+  decode_plan(Lplan, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.m_min);
+  da.nsplit = da.n_wsplit + 1;
+  da.layout = layout; da.R = R; da.page_shift = page_shift; da.num_pages = num_pages; da.max_pages = max_pages;
+  da.table = table;
+  hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+  return SA_OK;
+}
+
+int decode_head_checks(int B, int Hq, int Hkv, int L, int d, int dtype, int mode, int k_win, int pi, int M, int seg) {
+  int rc = check_shape(dtype, d);
+  if (rc != SA_OK) return rc;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and the cache length must be >= 1");
+  if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
+  return check_mode(mode, k_win, pi, M, seg);
+}
+
+// Rows a ring must keep: every key of the query at the newest position.
+long long ring_span(int mode, int k_win, int pi, int M, int seg) {
+  if (mode == SA_MODE_ECP) return 2LL * seg;
+  long long span = (long long)k_win + 1;
+  if (mode == SA_MODE_PI && M > 0 && (long long)M * pi + 1 > span) span = (long long)M * pi + 1;
+  return span;
+}
+
+int page_shift_of(int page_size) {
+  if (page_size < 8 || page_size > 4096 || (page_size & (page_size - 1)) != 0) return -1;
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  return sh;
+}
+
+}  // namespace
+
 int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,
                        const float *alpha, void *o, int B, int Hq, int Hkv, int Lmax, int d, int dtype, int mode,
                        int k_win, int pi, int M, int seg, void *workspace, size_t workspace_bytes, void *stream) {
   g_err[0] = 0;
-  int rc = check_shape(dtype, d);
+  int rc = decode_head_checks(B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi, M, seg);
   if (rc != SA_OK) return rc;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and Lmax must be >= 1");
-  if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
-  rc = check_mode(mode, k_win, pi, M, seg);
+  if ((long long)B * Hkv * Lmax >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
+  const size_t nc = (size_t)B * Hkv * Lmax * d * elem_size(dtype);
+  return decode_impl(q, k_cache, v_cache, nullptr, cache_lens, alpha, o, B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi,
+                     M, seg, sa::kCacheContig, 0, 0, 0, 0, nc, workspace, workspace_bytes, stream);
+}
+
+size_t sparse_attn_decode_ring_workspace_size(int B, int Hq, int Hkv, int R, int d, int dtype, int mode, int k_win,
+                                              int pi, int M, int seg) {
+  if (dtype != SA_DTYPE_BF16 || check_mode(mode, k_win, pi, M, seg) != SA_OK ||
+      R < ring_span(mode, k_win, pi, M, seg))
+    return 0;
+  return sparse_attn_decode_workspace_size(B, Hq, Hkv, R, d, dtype, mode, k_win, pi, M, seg);
+}
+
+int sparse_attn_decode_ring(const void *q, const void *k_ring, const void *v_ring, const int *cache_lens,
+                            const float *alpha, void *o, int B, int Hq, int Hkv, int R, int d, int dtype, int mode,
+                            int k_win, int pi, int M, int seg, void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  int rc = decode_head_checks(B, Hq, Hkv, R, d, dtype, mode, k_win, pi, M, seg);
   if (rc != SA_OK) return rc;
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || o == nullptr)
-    return fail(SA_ERR_INVALID, "null tensor pointer");
-  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-      !aligned(alpha, 4) || !aligned(cache_lens, 4))
-    return fail(SA_ERR_INVALID, "misaligned tensor");
-  if ((long long)B * Hkv * Lmax >= (1LL << 31) || (long long)Lmax * d >= (1LL << 31) || B > 65535)
-    return fail(SA_ERR_INVALID, "problem too large");
-  const size_t need = sparse_attn_decode_workspace_size(B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi, M, seg);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_decode_workspace_size()");
-  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
-  const size_t es = elem_size(dtype);
-  const size_t nq = (size_t)B * Hq * d * es, nc = (size_t)B * Hkv * Lmax * d * es;
-  if (overlap(o, nq, q, nq) || overlap(o, nq, k_cache, nc) || overlap(o, nq, v_cache, nc) ||
-      overlap(o, nq, alpha, alpha ? (size_t)B * Hq * 4 : 0) || overlap(o, nq, cache_lens, (size_t)B * 4) ||
-      overlap(o, nq, workspace, need))
-    return fail(SA_ERR_INVALID, "output overlaps an input or the workspace");
-  sa::DecodeArgs da;
-  da.q = q; da.kc = k_cache; da.vc = v_cache; da.lens = cache_lens; da.alpha = alpha; da.o = o;
-  da.ws = (float *)workspace;
-  da.B = B; da.Hq = Hq; da.Hkv = Hkv; da.Lmax = Lmax; da.d = d; da.dtype = dtype;
-  da.mode = mode; da.k_win = k_win; da.pi = pi; da.M = M; da.seg = seg;
-  decode_plan(Lmax, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.m_min);
-  da.nsplit = da.n_wsplit + 1;
-  hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
-  return SA_OK;
+  if (dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "ring caches take bf16 I/O");
+  if (R < ring_span(mode, k_win, pi, M, seg))
+    return fail(SA_ERR_INVALID, "ring smaller than the key span (k_win + 1, M*pi + 1 or 2*seg)");
+  if ((long long)B * Hkv * R >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
+  const size_t nc = (size_t)B * Hkv * R * d * 2;
+  return decode_impl(q, k_ring, v_ring, nullptr, cache_lens, alpha, o, B, Hq, Hkv, R, d, dtype, mode, k_win, pi, M,
+                     seg, sa::kCacheRing, R, 0, 0, 0, nc, workspace, workspace_bytes, stream);
+}
+
+size_t sparse_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int max_pages, int d, int dtype,
+                                               int mode, int k_win, int pi, int M, int seg) {
+  const int sh = page_shift_of(page_size);
+  if (dtype != SA_DTYPE_BF16 || sh < 0 || max_pages <= 0 || (long long)max_pages * page_size >= (1LL << 31) ||
+      (mode == SA_MODE_PI && M > 63))
+    return 0;
+  return sparse_attn_decode_workspace_size(B, Hq, Hkv, max_pages * page_size, d, dtype, mode, k_win, pi, M, seg);
+}
+
+int sparse_attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int *block_table,
+                             const int *cache_lens, const float *alpha, void *o, int B, int Hq, int Hkv,
+                             int num_pages, int page_size, int max_pages, int d, int dtype, int mode, int k_win,
+                             int pi, int M, int seg, void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  const int sh = page_shift_of(page_size);
+  if (sh < 0) return fail(SA_ERR_INVALID, "page_size must be a power of two in [8, 4096]");
+  if (max_pages <= 0 || num_pages <= 0) return fail(SA_ERR_INVALID, "num_pages and max_pages must be >= 1");
+  if ((long long)max_pages * page_size >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
+  int rc = decode_head_checks(B, Hq, Hkv, max_pages * page_size, d, dtype, mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  if (dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "paged caches take bf16 I/O");
+  if (mode == SA_MODE_PI && M > 63) return fail(SA_ERR_UNSUPPORTED, "paged caches take M <= 63");
+  if ((long long)num_pages * Hkv * page_size >= (1LL << 31)) return fail(SA_ERR_INVALID, "page pool too large");
+  const size_t nc = (size_t)num_pages * Hkv * page_size * d * 2;
+  return decode_impl(q, k_pages, v_pages, block_table, cache_lens, alpha, o, B, Hq, Hkv, max_pages * page_size, d,
+                     dtype, mode, k_win, pi, M, seg, sa::kCachePaged, 0, sh, num_pages, max_pages, nc, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t sparse_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win,

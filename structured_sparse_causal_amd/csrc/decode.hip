@@ -37,6 +37,8 @@ struct Params {
   int Hq, Hkv, Lmax, mode, k_win, pi, M, seg, m_min;
   int n_wsplit, chunk, nsplit, hchunks, grp;
   float scale_log2;
+  int R, page_shift, num_pages, max_pages;   // ring / paged cache layouts
+  const int *table;
 };
 
 
@@ -76,6 +78,78 @@ __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int spli
   return sr;
 }
 
+// Physical row (relative to the per-layout base pointer) of row r of a split.
+//   contiguous [B,Hkv,Lmax,d]: base = (b,g) slice, row = position;
+//   ring [B,Hkv,R,d]: base = (b,g) slice, row = position mod R (a split's rows
+//     are base + r*step with |r*step| < R, so one wrap of the slot of `base`);
+//   paged [num_pages,Hkv,P,d]: base = pool, row = (page*Hkv + g)*P + position % P,
+//     the page read by lane shuffle from the split's block-table entries that
+//     each wave loads up front (lane l: page l of a window split, or the page of
+//     row l of the query/skip split).
+template <int LAYOUT>
+struct RowMap {
+  SplitRows sr;
+  int sbase, qslot, R;             // ring
+  int ptab, page0, g, Hkv, P, sh;  // paged
+  __device__ __forceinline__ int phys(int r) const {
+    if constexpr (LAYOUT == kCacheContig) {
+      return sr.pos(r);
+    } else if constexpr (LAYOUT == kCacheRing) {
+      int x = sbase + r * sr.step;
+      x = x < 0 ? x + R : x;
+      x = x >= R ? x - R : x;
+      return (sr.last && r == 0) ? qslot : x;
+    } else {
+      const int pos = sr.pos(r);
+      const int idx = sr.last ? r : (pos >> sh) - page0;
+      const int page = __shfl(ptab, idx, 64);
+      return (page * Hkv + g) * P + (pos & (P - 1));
+    }
+  }
+};
+
+__device__ __forceinline__ int mod_pos(long long x, int R) {
+  const long long m = x % R;
+  return (int)(m < 0 ? m + R : m);
+}
+
+// Builds the row map of a split; `bad` is set (uniformly across the
+// workgroup) when a block-table entry the split needs is out of range.
+template <int LAYOUT>
+__device__ __forceinline__ RowMap<LAYOUT> make_rowmap(const Params &p, const SplitRows &sr, int b, int g, int lane,
+                                                      bool &bad) {
+  RowMap<LAYOUT> rm;
+  rm.sr = sr;
+  bad = false;
+  if constexpr (LAYOUT == kCacheRing) {
+    rm.R = p.R;
+    rm.sbase = mod_pos(sr.base, p.R);
+    rm.qslot = mod_pos(sr.qrow, p.R);
+  } else if constexpr (LAYOUT == kCachePaged) {
+    rm.g = g;
+    rm.Hkv = p.Hkv;
+    rm.sh = p.page_shift;
+    rm.P = 1 << p.page_shift;
+    rm.page0 = sr.base >> p.page_shift;
+    rm.ptab = 0;
+    if (sr.count > 0) {
+      int pg;
+      bool need;
+      if (!sr.last) {
+        pg = rm.page0 + lane;
+        need = pg <= ((sr.base + sr.count - 1) >> p.page_shift);
+      } else {
+        need = lane < sr.count;
+        pg = sr.pos(need ? lane : 0) >> p.page_shift;
+      }
+      const int e = need ? p.table[(size_t)b * p.max_pages + pg] : 0;
+      rm.ptab = e;
+      bad = __any(need && (e < 0 || e >= p.num_pages));
+    }
+  }
+  return rm;
+}
+
 constexpr int kWaves = 4;
 constexpr int kRing = 2;   // 16-row groups per wave held in registers (kRing - 1 in flight)
 
@@ -95,15 +169,15 @@ struct Group {
 // compiler wait on each load right after issuing it): rows past the split's
 // end re-read its last row (scores masked, probabilities 0) and an empty split
 // reads `fallback`, an in-range row.
-template <int D>
-__device__ __forceinline__ Group<D> load_group(const bf16 *Kp, const bf16 *Vp, const SplitRows &sr, int r0,
+template <int D, int LAYOUT>
+__device__ __forceinline__ Group<D> load_group(const bf16 *Kp, const bf16 *Vp, const RowMap<LAYOUT> &rm, int r0,
                                                int lane, int fallback) {
   Group<D> g;
-  const int last = sr.count - 1;
+  const int last = rm.sr.count - 1;
 #pragma unroll
   for (int u = 0; u < Group<D>::NC; ++u) {
     const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-    const size_t off = (size_t)(last >= 0 ? sr.pos(min(r0 + row, last)) : fallback) * D + col;
+    const size_t off = (size_t)(last >= 0 ? rm.phys(min(r0 + row, last)) : fallback) * D + col;
     g.k[u] = load_once16(Kp + off);
     g.v[u] = load_once16(Vp + off);
   }
@@ -270,7 +344,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(Params p) {
 // more waves fit per SIMD.  HC4 = 4-head chunks per workgroup (heads of the
 // group handled by one workgroup, up to 16).
 // ---------------------------------------------------------------------------
-template <int D, int HC4>
+template <int D, int HC4, int LAYOUT>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   // Per-wave slabs of the group's 16 rows.  K: row stride 16 bytes mod 256,
   // so the 16 rows of an A-fragment read hit distinct banks.  V: row stride
@@ -293,18 +367,27 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   const int g = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
   const int b = blockIdx.z;
   const int len = p.lens[b];
-  const bool len_ok = len >= 1 && len <= p.Lmax;
+  // a ring cache holds any number of written tokens (the last R of them)
+  bool len_ok = len >= 1 && (LAYOUT == kCacheRing || len <= p.Lmax);
   const int i = len_ok ? len - 1 : 0;
   const int head = 16 * hc + t;               // score column t = head of the group
   const bool hvalid = head < p.grp && t < NHD;
   const int hq = g * p.grp + head;
-  const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lmax * D;
+  const size_t kvoff = LAYOUT == kCachePaged ? 0
+                       : (size_t)(b * p.Hkv + g) * (LAYOUT == kCacheRing ? p.R : p.Lmax) * D;
   const bf16 *Kp = (const bf16 *)p.kc + kvoff;
   const bf16 *Vp = (const bf16 *)p.vc + kvoff;
   const bf16 *Qp = (const bf16 *)p.q + ((size_t)b * p.Hq + hq) * D;
 
   SplitRows sr = split_rows(p, i, split);
   if (!len_ok) sr.count = 0;
+  bool bad_page;
+  const RowMap<LAYOUT> rm = make_rowmap<LAYOUT>(p, sr, b, g, lane, bad_page);
+  if (bad_page) {   // an unmapped page: NaN output, no cache access
+    len_ok = false;
+    sr.count = 0;
+  }
+  const int fallback = LAYOUT == kCacheContig ? i : 0;   // an in-range physical row
 
   float bias_loc = 0.f, bias_skip = 0.f;   // log2 priors of local and skip keys
   if (p.mode == kModePi && p.alpha != nullptr && hvalid) {
@@ -407,11 +490,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   constexpr int kStep = 16 * kWaves;
   Group<D> ring[kRing];
 #pragma unroll
-  for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, sr, 16 * wave + j * kStep, lane, i);
+  for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, rm, 16 * wave + j * kStep, lane, fallback);
   for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {
-      ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, sr, r0 + (j + kRing - 1) * kStep, lane, i);
+      ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, rm, r0 + (j + kRing - 1) * kStep, lane, fallback);
       if (r0 + j * kStep < sr.count) consume(ring[j], r0 + j * kStep);
     }
   }
@@ -519,13 +602,25 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   p.grp = a.Hq / a.Hkv;
   p.hchunks = (p.grp + 15) / 16;
   p.scale_log2 = kLog2e / sqrtf((float)D);
+  p.R = a.R; p.page_shift = a.page_shift; p.num_pages = a.num_pages; p.max_pages = a.max_pages; p.table = a.table;
   const dim3 grid(p.nsplit, a.Hkv * p.hchunks, a.B);
   if constexpr (sizeof(T) == 2) {
     const int heads = p.grp < 16 ? p.grp : 16;   // heads per workgroup
-    if (heads <= 4) hipLaunchKernelGGL((decode_bf16_kernel<D, 1>), grid, dim3(256), 0, s, p);
-    else if (heads <= 8) hipLaunchKernelGGL((decode_bf16_kernel<D, 2>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((decode_bf16_kernel<D, 4>), grid, dim3(256), 0, s, p);
+    const int hc4 = heads <= 4 ? 1 : heads <= 8 ? 2 : 4;
+#define SA_DECODE_LAUNCH(L)                                                                  \
+  if (hc4 == 1) hipLaunchKernelGGL((decode_bf16_kernel<D, 1, L>), grid, dim3(256), 0, s, p); \
+  else if (hc4 == 2) hipLaunchKernelGGL((decode_bf16_kernel<D, 2, L>), grid, dim3(256), 0, s, p); \
+  else hipLaunchKernelGGL((decode_bf16_kernel<D, 4, L>), grid, dim3(256), 0, s, p);
+    if (a.layout == kCacheRing) {
+      SA_DECODE_LAUNCH(kCacheRing)
+    } else if (a.layout == kCachePaged) {
+      SA_DECODE_LAUNCH(kCachePaged)
+    } else {
+      SA_DECODE_LAUNCH(kCacheContig)
+    }
+#undef SA_DECODE_LAUNCH
   } else {
+    if (a.layout != kCacheContig) return hipErrorInvalidValue;   // fp32: contiguous caches only
     hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();

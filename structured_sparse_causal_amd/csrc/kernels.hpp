@@ -44,7 +44,13 @@ struct DecodeArgs {
   int B, Hq, Hkv, Lmax, d, dtype;
   int mode, k_win, pi, M, seg, m_min;
   int n_wsplit, chunk, nsplit;   // window splits, rows per window split, n_wsplit + 1
+  // Cache layout: kCacheContig kc/vc [B,Hkv,Lmax,d]; kCacheRing kc/vc [B,Hkv,R,d]
+  // with position p in slot p mod R; kCachePaged kc/vc [num_pages,Hkv,P,d] with
+  // block table [B][max_pages] (P = 1 << page_shift, Lmax = max_pages * P).
+  int layout, R, page_shift, num_pages, max_pages;
+  const int *table;
 };
+enum { kCacheContig = 0, kCacheRing = 1, kCachePaged = 2 };
 
 struct BwdArgs {
   const void *q, *k, *v, *o, *dO;   // bf16

@@ -201,3 +201,66 @@ def test_bwd_workspace_sizes(lib):
     assert ws(1, 2, 2, 256, 64, BF16, ECP, 0, 0, 0, 64) == 2 * r256((512 + 16) * 4)
     assert ws(1, 2, 2, 256, 64, F32, WINDOW, 8, 0, 0, 0) == 0                        # bf16 only
     assert ws(1, 2, 2, 256, 80, BF16, WINDOW, 8, 0, 0, 0) == 0
+
+
+def ring(lib, q=Q, kr=K, vr=V, lens=A, a=A + 4096, o=O, B=2, Hq=8, Hkv=2, R=512, d=128, dtype=BF16,
+         mode=PI, k_win=64, pi=64, M=3, seg=0, ws=WS, wsb=1 << 30):
+    return lib.sparse_attn_decode_ring(q, kr, vr, lens, a, o, B, Hq, Hkv, R, d, dtype, mode, k_win, pi, M, seg,
+                                       ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), UNSUPPORTED), (dict(d=80), UNSUPPORTED), (dict(R=0), INVALID),
+    (dict(R=192), INVALID),                        # M*pi + 1 = 193 rows must stay resident
+    (dict(mode=WINDOW, k_win=600), INVALID),       # k_win + 1 = 601 > R
+    (dict(mode=ECP, seg=300), INVALID),            # 2*seg = 600 > R
+    (dict(lens=None), INVALID), (dict(a=None), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(o=K + 128), INVALID), (dict(ws=WS + 64), INVALID),
+])
+def test_decode_ring_rejects(lib, kw, code):
+    assert ring(lib, **kw) == code
+
+
+def test_decode_ring_accepts_minimal_span(lib):
+    # R = M*pi + 1 exactly is valid: validation passes and stops at the
+    # overlapping output.
+    assert ring(lib, R=193, o=Q) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+
+
+def test_decode_ring_workspace_size(lib):
+    ws = lib.sparse_attn_decode_ring_workspace_size
+    # planned like a contiguous cache of R rows
+    assert ws(64, 32, 8, 30721, 128, BF16, PI, 2048, 2048, 15, 0) == \
+        lib.sparse_attn_decode_workspace_size(64, 32, 8, 30721, 128, BF16, PI, 2048, 2048, 15, 0) > 0
+    assert ws(64, 32, 8, 30720, 128, BF16, PI, 2048, 2048, 15, 0) == 0      # ring too short
+    assert ws(2, 8, 2, 512, 128, F32, WINDOW, 64, 0, 0, 0) == 0             # bf16 only
+
+
+TAB = 0x30000000
+
+
+def paged(lib, q=Q, kp=K, vp=V, tab=TAB, lens=A, a=A + 4096, o=O, B=2, Hq=8, Hkv=2, num_pages=64, P=64,
+          max_pages=16, d=128, dtype=BF16, mode=PI, k_win=64, pi=64, M=3, seg=0, ws=WS, wsb=1 << 30):
+    return lib.sparse_attn_decode_paged(q, kp, vp, tab, lens, a, o, B, Hq, Hkv, num_pages, P, max_pages, d, dtype,
+                                        mode, k_win, pi, M, seg, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(P=48), INVALID), (dict(P=4), INVALID),
+    (dict(P=8192), INVALID), (dict(max_pages=0), INVALID), (dict(num_pages=0), INVALID),
+    (dict(M=64), UNSUPPORTED), (dict(tab=None), INVALID), (dict(tab=TAB + 2), INVALID),
+    (dict(o=TAB), INVALID), (dict(ws=None), WORKSPACE), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(num_pages=1 << 20, Hkv=64, Hq=64), INVALID),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert paged(lib, **kw) == code
+
+
+def test_decode_paged_workspace_size(lib):
+    ws = lib.sparse_attn_decode_paged_workspace_size
+    # planned like a contiguous cache of max_pages * page_size rows
+    assert ws(64, 32, 8, 64, 512, 128, BF16, PI, 2048, 2048, 15, 0) == \
+        lib.sparse_attn_decode_workspace_size(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0)
+    assert ws(1, 1, 1, 48, 4, 64, BF16, WINDOW, 8, 0, 0, 0) == 0           # page size not a power of two
+    assert ws(1, 1, 1, 64, 4, 64, F32, WINDOW, 8, 0, 0, 0) == 0
