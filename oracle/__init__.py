@@ -34,7 +34,11 @@ import numpy as np
 MODE_PI = 0
 MODE_WINDOW = 1
 MODE_ECP = 2
-MODES = {"pi": MODE_PI, "window": MODE_WINDOW, "ecp": MODE_ECP}
+MODE_WINDOW_BIDIR = 3
+MODE_SSPLIT = 4
+MODE_ECP_FULL = 5
+MODES = {"pi": MODE_PI, "window": MODE_WINDOW, "ecp": MODE_ECP, "window_bidir": MODE_WINDOW_BIDIR,
+         "ssplit": MODE_SSPLIT, "ecp_full": MODE_ECP_FULL}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sparse_attn_oracle.c")
@@ -63,7 +67,7 @@ def _load():
             lib = ctypes.CDLL(_LIB)
             i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
             lib.orc_key_set.restype = i64
-            lib.orc_key_set.argtypes = [i64, i32, i64, i64, i64, i64, vp, vp, i64]
+            lib.orc_key_set.argtypes = [i64, i64, i32, i64, i64, i64, i64, vp, vp, i64]
             lib.orc_key_capacity.restype = i64
             lib.orc_key_capacity.argtypes = [i32, i64, i64, i64]
             lib.orc_fwd_rows.restype = i32
@@ -114,15 +118,17 @@ def set_num_threads(n: int) -> None:
     _load().orc_set_num_threads(int(n))
 
 
-def key_set(i: int, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0):
-    """Key set of query position ``i`` as (positions, labels); label 0 = local,
-    1 = skip.  pi-Attention section 2 items 1-2; ECP section 2; LT2 section 2.1."""
+def key_set(i: int, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0, N=None):
+    """Key set of query position ``i`` of an N-position sequence (default
+    N = i + 1, enough for the causal modes) as (positions, labels); label
+    0 = local, 1 = skip.  pi-Attention section 2 items 1-2; ECP section 2;
+    LT2 section 2.1."""
     lib = _load()
     m = _mode(mode)
     cap = max(1, lib.orc_key_capacity(m, k_win, M, seg))
     keys = np.zeros(cap, dtype=np.int64)
     labels = np.zeros(cap, dtype=np.int32)
-    n = lib.orc_key_set(int(i), m, int(k_win), int(pi), int(M), int(seg),
+    n = lib.orc_key_set(int(i), int(i) + 1 if N is None else int(N), m, int(k_win), int(pi), int(M), int(seg),
                         keys.ctypes.data, labels.ctypes.data, cap)
     if n < 0:
         raise ValueError("oracle: invalid key-set parameters")

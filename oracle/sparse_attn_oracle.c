@@ -28,6 +28,14 @@
  *     section 2, PAR block): a query in half-segment c = floor(i/s) sees the
  *     keys of half-segments c-1 and c, causally masked, i.e.
  *     j in [max(0, (c-1)*s), i].  No prior.
+ *   - Further masks on the same machinery (no prior, N = sequence length):
+ *       window_bidir: j in [max(0, i-k), min(N-1, i+k)] -- the local window
+ *         exactly as the pi-Attention page states it, i-k..i+k (encoder use);
+ *       ssplit: j in [floor(i/s)*s, i] -- the s-Split variant of the ECP page
+ *         (section 2): the history cut into disjoint segments, causal inside;
+ *       ecp_full: j in [max(0, (c-1)*s), min(N-1, (c+1)*s - 1)] -- the PAR
+ *         block of the ECP page without the causal restriction (queries of
+ *         half-segment c see all of half-segments c-1 and c).
  *
  *   score(i, j) = <q_i, k_j> / sqrt(d) + prior(i, j)
  *   o_i        = sum_j exp(score(i,j) - max) v_j / sum_j exp(score(i,j) - max)
@@ -48,6 +56,9 @@
 #define ORC_MODE_PI 0
 #define ORC_MODE_WINDOW 1
 #define ORC_MODE_ECP 2
+#define ORC_MODE_WINDOW_BIDIR 3
+#define ORC_MODE_SSPLIT 4
+#define ORC_MODE_ECP_FULL 5
 
 #define ORC_LOCAL 0
 #define ORC_SKIP 1
@@ -58,34 +69,44 @@
 #define ORC_ERR_NOMEM -3
 
 static int64_t orc_max64(int64_t a, int64_t b) { return a > b ? a : b; }
+static int64_t orc_min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
 /* Number of keys the key set of any query can hold (upper bound). */
 int64_t orc_key_capacity(int mode, int64_t k_win, int64_t M, int64_t seg)
 {
-    if (mode == ORC_MODE_ECP) return 2 * seg;
+    if (mode == ORC_MODE_ECP || mode == ORC_MODE_ECP_FULL) return 2 * seg;
+    if (mode == ORC_MODE_SSPLIT) return seg;
     if (mode == ORC_MODE_WINDOW) return k_win + 1;
+    if (mode == ORC_MODE_WINDOW_BIDIR) return 2 * k_win + 1;
     return k_win + 1 + (M > 0 ? M : 0);
 }
 
 /*
- * Key set of query position i, in ascending order of position, with the
- * label ORC_LOCAL or ORC_SKIP for each key.  Returns the number of keys, or
- * -1 when cap is too small or the parameters are invalid.
+ * Key set of query position i of a sequence of N positions, in ascending
+ * order of position, with the label ORC_LOCAL or ORC_SKIP for each key.
+ * Returns the number of keys, or -1 when cap is too small or the parameters
+ * are invalid.
  *   PI / WINDOW: pi-Attention section 2 items 1-2; LT2 section 2.1.
  *   ECP: ECP section 2 (queries of the current half-segment, keys and values
  *   of the current and the previous half-segment), causal.
+ *   WINDOW_BIDIR, SSPLIT, ECP_FULL: see the header comment.
  */
-int64_t orc_key_set(int64_t i, int mode, int64_t k_win, int64_t pi, int64_t M,
+int64_t orc_key_set(int64_t i, int64_t N, int mode, int64_t k_win, int64_t pi, int64_t M,
                     int64_t seg, int64_t *keys, int32_t *labels, int64_t cap)
 {
-    int64_t n = 0, lo, j, m;
-    if (i < 0) return -1;
-    if (mode == ORC_MODE_ECP) {
+    int64_t n = 0, lo, hi = i, j, m;
+    if (i < 0 || i >= N) return -1;
+    if (mode == ORC_MODE_ECP || mode == ORC_MODE_ECP_FULL) {
         if (seg <= 0) return -1;
         lo = orc_max64(0, (i / seg - 1) * seg);
-    } else if (mode == ORC_MODE_PI || mode == ORC_MODE_WINDOW) {
+        if (mode == ORC_MODE_ECP_FULL) hi = orc_min64(N - 1, (i / seg + 1) * seg - 1);
+    } else if (mode == ORC_MODE_SSPLIT) {
+        if (seg <= 0) return -1;
+        lo = (i / seg) * seg;
+    } else if (mode == ORC_MODE_PI || mode == ORC_MODE_WINDOW || mode == ORC_MODE_WINDOW_BIDIR) {
         if (k_win < 0) return -1;
         lo = orc_max64(0, i - k_win);
+        if (mode == ORC_MODE_WINDOW_BIDIR) hi = orc_min64(N - 1, i + k_win);
     } else {
         return -1;
     }
@@ -103,7 +124,7 @@ int64_t orc_key_set(int64_t i, int mode, int64_t k_win, int64_t pi, int64_t M,
             ++n;
         }
     }
-    for (j = lo; j <= i; ++j) {
+    for (j = lo; j <= hi; ++j) {
         if (n >= cap) return -1;
         keys[n] = j;
         labels[n] = ORC_LOCAL;
@@ -147,8 +168,9 @@ static int orc_check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int m
                             int64_t k_win, int64_t pi, int64_t M, int64_t seg)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return ORC_ERR_ARGS;
-    if (mode == ORC_MODE_ECP) return seg > 0 ? ORC_OK : ORC_ERR_ARGS;
-    if (mode != ORC_MODE_PI && mode != ORC_MODE_WINDOW) return ORC_ERR_ARGS;
+    if (mode == ORC_MODE_ECP || mode == ORC_MODE_SSPLIT || mode == ORC_MODE_ECP_FULL)
+        return seg > 0 ? ORC_OK : ORC_ERR_ARGS;
+    if (mode != ORC_MODE_PI && mode != ORC_MODE_WINDOW && mode != ORC_MODE_WINDOW_BIDIR) return ORC_ERR_ARGS;
     if (k_win < 0) return ORC_ERR_ARGS;
     if (mode == ORC_MODE_PI && (M < 0 || (M > 0 && pi <= 0))) return ORC_ERR_ARGS;
     return ORC_OK;
@@ -207,7 +229,7 @@ int orc_fwd_rows(const float *q, const float *k, const float *v, const float *al
             b = row / (N * Hq);
             g = h / (Hq / Hkv);
             if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) continue;
-            n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+            n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             orc_row(q + row * d, k + (b * Hkv + g) * N * d, v + (b * Hkv + g) * N * d,
                     d, lp, ls, keys, labels, n, score, out + r * d);
@@ -239,6 +261,8 @@ int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *
     int64_t cap, r;
     int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
     if (err != ORC_OK || Lmax <= 0) return ORC_ERR_ARGS;
+    /* a decoded token has no later keys: the non-causal masks do not apply */
+    if (mode == ORC_MODE_WINDOW_BIDIR || mode == ORC_MODE_ECP_FULL) return ORC_ERR_ARGS;
     for (r = 0; r < B; ++r)
         if (lens[r] < 1 || lens[r] > Lmax) return ORC_ERR_ARGS;
     cap = orc_key_capacity(mode, k_win, M, seg);
@@ -255,7 +279,7 @@ int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *
             double lp, ls;
             if (local_err != ORC_OK) continue;
             if ((local_err = orc_priors(mode, alpha, r, &lp, &ls)) != ORC_OK) continue;
-            n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+            n = orc_key_set(i, i + 1, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             orc_row(q + r * d, kc + (b * Hkv + g) * Lmax * d, vc + (b * Hkv + g) * Lmax * d,
                     d, lp, ls, keys, labels, n, score, out + r * d);
@@ -307,7 +331,7 @@ int orc_lse_rows(const float *q, const float *k, const float *alpha,
             b = row / (N * Hq);
             g = h / (Hq / Hkv);
             if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) continue;
-            n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+            n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             qrow = q + row * d;
             kmat = k + (b * Hkv + g) * N * d;
@@ -388,7 +412,7 @@ int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, 
                     const float *qrow = q + row * d, *dorow = dO + row * d;
                     double lp, ls, mx = -INFINITY, sum = 0.0, lse, D = 0.0, da = 0.0;
                     if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) break;
-                    n = orc_key_set(i, mode, k_win, pi, M, seg, keys, labels, cap);
+                    n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
                     if (n <= 0) { local_err = ORC_ERR_ARGS; break; }
                     for (t = 0; t < n; ++t) {
                         double dot = 0.0;
