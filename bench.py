@@ -92,9 +92,19 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
 # Useful work (attended pairs) and algorithmic bytes, from the mask definitions
 # ---------------------------------------------------------------------------
 def key_lo(i, w):
-    if w.mode == "ecp":
+    if w.mode in ("ecp", "ecp_full"):
         return np.maximum(0, (i // w.seg - 1) * w.seg)
+    if w.mode == "ssplit":
+        return (i // w.seg) * w.seg
     return np.maximum(0, i - w.k_win)
+
+
+def key_hi(i, w, N):
+    if w.mode == "window_bidir":
+        return np.minimum(N - 1, i + w.k_win)
+    if w.mode == "ecp_full":
+        return np.minimum(N - 1, (i // w.seg + 1) * w.seg - 1)
+    return i
 
 
 def pairs_per_head(w, N=None):
@@ -102,7 +112,7 @@ def pairs_per_head(w, N=None):
     plus, for pi-Attention, the skip keys lying below the window."""
     N = w.N if N is None else N
     i = np.arange(N, dtype=np.int64)
-    n = (i - key_lo(i, w) + 1).sum()
+    n = (key_hi(i, w, N) - key_lo(i, w) + 1).sum()
     if w.mode == "pi" and w.M > 0:
         lo = key_lo(i, w)
         for m in range(1, w.M + 1):
@@ -374,6 +384,11 @@ def main():
                               **run_decode_layouts(torch, sa, WORKLOADS["decode_pi_gqa_bf16"], args.steps,
                                                    args.warmup)}), flush=True)
             return
+        from structured_sparse_causal_amd.inputs import MASK_WORKLOADS
+        if args.only in MASK_WORKLOADS:
+            print(json.dumps({"workload": args.only, **run_prefill_workload(torch, sa, MASK_WORKLOADS[args.only],
+                                                                           args.steps, args.warmup)}), flush=True)
+            return
         if args.only.startswith("bwd_"):
             wx = WORKLOADS[args.only[4:]].replace(loops=1)
             print(json.dumps({"workload": args.only, **run_bwd_workload(torch, sa, wx, args.steps, args.warmup)}),
@@ -452,6 +467,13 @@ def main():
                 extras[name] = run_decode_workload(torch, sa, wx, reps, 3)
             else:
                 extras[name] = run_prefill_workload(torch, sa, wx, reps, 3)
+            log("  %s" % json.dumps(extras[name]))
+            torch.cuda.empty_cache()
+        # Further mask modes (forward), at the ECP and looped-window shapes.
+        from structured_sparse_causal_amd.inputs import MASK_WORKLOADS
+        for name, wx in MASK_WORKLOADS.items():
+            log("bench: mask mode %s" % name)
+            extras[name] = run_prefill_workload(torch, sa, wx, 10 if wx.d == 128 else 30, 3)
             log("  %s" % json.dumps(extras[name]))
             torch.cuda.empty_cache()
         # Serving decode: cache layouts, and throughput over cache lengths.

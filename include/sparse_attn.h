@@ -26,6 +26,17 @@
  *                   Language Modeling", section 2, PAR block): a query in
  *                   half-segment c = floor(i / seg) attends the keys of
  *                   half-segments c-1 and c, causally: [max(0,(c-1)*seg), i].
+ *   Further masks (no prior; prefill forward and backward, and decode where
+ *   the mask is causal):
+ *   SA_MODE_WINDOW_BIDIR  the two-sided window [max(0,i-k_win), min(N-1,i+k_win)],
+ *                   the local window exactly as the pi-Attention page states
+ *                   it (encoder use; not a decode mode).
+ *   SA_MODE_SSPLIT  s-Split segments (ECP page, section 2): the sequence cut
+ *                   into disjoint segments of seg positions, causal inside:
+ *                   [floor(i/seg)*seg, i].
+ *   SA_MODE_ECP_FULL  the PAR block without the causal restriction: a query in
+ *                   half-segment c attends all of half-segments c-1 and c,
+ *                   [max(0,(c-1)*seg), min(N-1,(c+1)*seg-1)] (not a decode mode).
  *
  * Grouped-query attention (the attention branch of the hybrid GSS-Transformer
  * page, methodology item 1): query head h reads key/value head
@@ -71,6 +82,9 @@ extern "C" {
 #define SA_MODE_PI 0
 #define SA_MODE_WINDOW 1
 #define SA_MODE_ECP 2
+#define SA_MODE_WINDOW_BIDIR 3
+#define SA_MODE_SSPLIT 4
+#define SA_MODE_ECP_FULL 5
 
 /* I/O element types. */
 #define SA_DTYPE_F32 0

@@ -16,7 +16,11 @@ import torch
 MODE_PI = 0
 MODE_WINDOW = 1
 MODE_ECP = 2
-_MODES = {"pi": MODE_PI, "window": MODE_WINDOW, "ecp": MODE_ECP}
+MODE_WINDOW_BIDIR = 3
+MODE_SSPLIT = 4
+MODE_ECP_FULL = 5
+_MODES = {"pi": MODE_PI, "window": MODE_WINDOW, "ecp": MODE_ECP, "window_bidir": MODE_WINDOW_BIDIR,
+          "ssplit": MODE_SSPLIT, "ecp_full": MODE_ECP_FULL}
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1

@@ -30,11 +30,12 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Common checks of the mode parameters.  Returns SA_OK or an error code.
 int check_mode(int mode, int k_win, int pi, int M, int seg) {
-  if (mode == SA_MODE_ECP) {
-    if (seg <= 0) return fail(SA_ERR_INVALID, "ECP mode needs seg >= 1");
+  if (mode == SA_MODE_ECP || mode == SA_MODE_SSPLIT || mode == SA_MODE_ECP_FULL) {
+    if (seg <= 0) return fail(SA_ERR_INVALID, "segment modes need seg >= 1");
     return SA_OK;
   }
-  if (mode != SA_MODE_PI && mode != SA_MODE_WINDOW) return fail(SA_ERR_INVALID, "unknown mode");
+  if (mode != SA_MODE_PI && mode != SA_MODE_WINDOW && mode != SA_MODE_WINDOW_BIDIR)
+    return fail(SA_ERR_INVALID, "unknown mode");
   if (k_win < 0) return fail(SA_ERR_INVALID, "k_win must be >= 0");
   if (mode == SA_MODE_PI) {
     if (M < 0) return fail(SA_ERR_INVALID, "M must be >= 0");
@@ -251,7 +252,7 @@ static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d, bool skips) {
 // more split holds the query row and the skip keys.
 static void decode_plan(int Lmax, int mode, int k_win, int pi, int M, int seg, int *n_wsplit, int *chunk,
                         int *m_min) {
-  long long range = mode == SA_MODE_ECP ? 2LL * seg : (long long)k_win + 1;
+  long long range = mode == SA_MODE_ECP ? 2LL * seg : mode == SA_MODE_SSPLIT ? (long long)seg : (long long)k_win + 1;
   if (range > Lmax) range = Lmax;
   const long long below = range - 1;
   const int n = (int)((below + 255) / 256);
@@ -265,7 +266,7 @@ static void decode_plan(int Lmax, int mode, int k_win, int pi, int M, int seg, i
 size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d, int dtype, int mode, int k_win,
                                          int pi, int M, int seg) {
   if (check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv != 0 ||
-      check_mode(mode, k_win, pi, M, seg) != SA_OK)
+      check_mode(mode, k_win, pi, M, seg) != SA_OK || mode == SA_MODE_WINDOW_BIDIR || mode == SA_MODE_ECP_FULL)
     return 0;
   int nw, chunk, mm;
   decode_plan(Lmax, mode, k_win, pi, M, seg, &nw, &chunk, &mm);
@@ -320,6 +321,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
 int decode_head_checks(int B, int Hq, int Hkv, int L, int d, int dtype, int mode, int k_win, int pi, int M, int seg) {
   int rc = check_shape(dtype, d);
   if (rc != SA_OK) return rc;
+  if (mode == SA_MODE_WINDOW_BIDIR || mode == SA_MODE_ECP_FULL)
+    return fail(SA_ERR_UNSUPPORTED, "a decoded token has no later keys: non-causal masks are prefill-only");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and the cache length must be >= 1");
   if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
   return check_mode(mode, k_win, pi, M, seg);
@@ -328,6 +331,7 @@ int decode_head_checks(int B, int Hq, int Hkv, int L, int d, int dtype, int mode
 // Rows a ring must keep: every key of the query at the newest position.
 long long ring_span(int mode, int k_win, int pi, int M, int seg) {
   if (mode == SA_MODE_ECP) return 2LL * seg;
+  if (mode == SA_MODE_SSPLIT) return seg;
   long long span = (long long)k_win + 1;
   if (mode == SA_MODE_PI && M > 0 && (long long)M * pi + 1 > span) span = (long long)M * pi + 1;
   return span;

@@ -429,11 +429,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  const int hi_wg = min(i0 + BM - 1, N - 1);
+  const int hi_i = key_hi(qi, N, p.mode, p.k_win, p.seg);
+  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
   const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
   const int ntiles = (hi_wg - t_begin) / BN + 1;
   const bool wave_live = q0 < N;
-  const int w_hi = min(q0 + 31, N - 1);
+  const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
+  const int w_hi_first = key_hi(min(q0, N - 1), N, p.mode, p.k_win, p.seg);
   const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
   const int w_lo_last = key_lo(min(q0 + 31, N - 1), p.mode, p.k_win, p.seg);
   const bool w_allvalid = q0 + 31 < N;
@@ -469,8 +471,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], dp[kb], 0, 0, 0);
         }
       }
-      const bool full = w_allvalid && (j0 + BN - 1 <= q0) && (j0 >= w_lo_last);
-      const int a0 = lo_i - j0 - 4 * h, span = qi - lo_i;
+      const bool full = w_allvalid && (j0 + BN - 1 <= w_hi_first) && (j0 >= w_lo_last);
+      const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -505,9 +507,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   if (p.dalpha != nullptr && !seeded && h == 0) p.dalpha[row] = 0.f;
 }
 
-// Last query position that has key j in its window / ECP range (at most N - 1).
+// Queries whose key range [key_lo(i), key_hi(i)] holds key j form the range
+// [first_query(j), last_query(j)] (both ends of the key range are
+// non-decreasing in i), clipped to [0, N-1].
+__device__ __forceinline__ int first_query(int j, const Params &p) {
+  long long f = j;
+  if (p.mode == kModeWindowBidir) f = (long long)j - p.k_win;
+  else if (p.mode == kModeEcpFull) f = (long long)(j / p.seg) * p.seg;
+  return f > 0 ? (int)f : 0;
+}
+
 __device__ __forceinline__ int last_query(int j, const Params &p) {
-  const long long last = p.mode == kModeEcp ? ((long long)(j / p.seg) + 2) * p.seg - 1 : (long long)j + p.k_win;
+  long long last;
+  if (p.mode == kModeEcp || p.mode == kModeEcpFull) last = ((long long)(j / p.seg) + 2) * p.seg - 1;
+  else if (p.mode == kModeSsplit) last = ((long long)(j / p.seg) + 1) * p.seg - 1;
+  else last = (long long)j + p.k_win;   // pi-Attention window, window, two-sided window
   return last < p.N - 1 ? (int)last : p.N - 1;
 }
 
@@ -544,15 +558,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
   const int kw_last = min(j_w + 31, N - 1);
   const bool wave_live = j_w < N;
   const int hi_q = last_query(min(k0 + BM - 1, N - 1), p);
-  const int t_begin = k0;                       // the first query that can see key k0 is k0
+  const int t_begin = (first_query(k0, p) / BN) * BN;
   const int ntiles = (hi_q - t_begin) / BN + 1;
   const int wq_hi = last_query(kw_last, p);   // last query seeing this wave's keys
   const int w_lq_first = last_query(min(j_w, N - 1), p);   // last query seeing all of them
+  const int w_fq_first = first_query(min(j_w, N - 1), p);  // first query seeing any of them
+  const int w_fq_last = first_query(kw_last, p);            // first query seeing all of them
   const bool w_allvalid = j_w + 31 < N;
-  // Query iq sees key kj iff kj <= iq <= last_query(kj) (key_lo is
-  // non-decreasing in iq); an invalid key gets an empty range.
-  const int vis_lo = kvalid ? kj : -(1 << 30);
-  const unsigned vis_span = kvalid ? (unsigned)(last_query(kj, p) - kj) : 0u;
+  // Query iq sees key kj iff first_query(kj) <= iq <= last_query(kj); an
+  // invalid key gets an empty range.
+  const int vis_lo = kvalid ? first_query(kj, p) : -(1 << 30);
+  const unsigned vis_span = kvalid ? (unsigned)(last_query(kj, p) - first_query(kj, p)) : 0u;
   const TileOffsets<D> off(lane);
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
   const float *cl = (const float *)(smem + 4 * TILE);       // [2][64] c, then [2][64] D
@@ -583,13 +599,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
         stage_vec(Cp, i0 + BN, lds0 + 4 * TILE + 256 * (buf ^ 1));
         stage_vec(Dp, i0 + BN, lds0 + 4 * TILE + 512 + 256 * (buf ^ 1));
       }
-      // this wave's keys [j_w, kw_last] are seen by queries [j_w, wq_hi]
-      if (wave_live && i0 + BN - 1 >= j_w && i0 <= wq_hi) {
+      // this wave's keys [j_w, kw_last] are seen by queries [w_fq_first, wq_hi]
+      if (wave_live && i0 + BN - 1 >= w_fq_first && i0 <= wq_hi) {
         const char *QB = smem + buf * TILE;
         const char *OB = smem + (2 + buf) * TILE;
         const float *cq = cl + 64 * buf, *dq = cl + 128 + 64 * buf;
         // every (query, key) of the tile visible: no per-element mask
-        const bool full = w_allvalid && i0 >= kw_last && i0 + BN - 1 <= w_lq_first;
+        const bool full = w_allvalid && i0 >= w_fq_last && i0 + BN - 1 <= w_lq_first;
         // The 64 queries in two halves of 32 (fewer live accumulators).
 #pragma unroll
         for (int qb2 = 0; qb2 < 2; ++qb2) {

@@ -86,16 +86,28 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-// First key position of query i's window (window / pi-Attention: [i-k, i]) or
-// paired half-segments (ECP: [(floor(i/s)-1)*s, i]), clipped at 0.  Mode
-// numbers as in kernels.hpp (kModeEcp = 2).
+// Key range [key_lo(i), key_hi(i)] of query i (mode numbers as in kernels.hpp):
+//   0 pi-Attention window / 1 window:  [max(0, i-k), i]
+//   2 ECP paired half-segments:        [max(0, (floor(i/s)-1)*s), i]
+//   3 two-sided window:                [max(0, i-k), min(N-1, i+k)]
+//   4 s-Split disjoint segments:       [floor(i/s)*s, i]
+//   5 ECP pair without causal mask:    [max(0, (floor(i/s)-1)*s), min(N-1, (floor(i/s)+1)*s - 1)]
+// Both ends are non-decreasing in i.
 __device__ __forceinline__ int key_lo(int i, int mode, int k_win, int seg) {
-  if (mode == 2) {
+  if (mode == 2 || mode == 5) {
     const int lo = (i / seg - 1) * seg;
     return lo > 0 ? lo : 0;
   }
+  if (mode == 4) return (i / seg) * seg;
   const int lo = i - k_win;
   return lo > 0 ? lo : 0;
+}
+
+__device__ __forceinline__ int key_hi(int i, int N, int mode, int k_win, int seg) {
+  long long hi = i;
+  if (mode == 3) hi = (long long)i + k_win;
+  else if (mode == 5) hi = ((long long)(i / seg) + 1) * seg - 1;
+  return hi < N - 1 ? (int)hi : N - 1;
 }
 
 __device__ __forceinline__ float half_swap_max(float x) {

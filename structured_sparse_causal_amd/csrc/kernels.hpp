@@ -7,7 +7,7 @@
 
 namespace sa {
 
-enum { kModePi = 0, kModeWindow = 1, kModeEcp = 2 };
+enum { kModePi = 0, kModeWindow = 1, kModeEcp = 2, kModeWindowBidir = 3, kModeSsplit = 4, kModeEcpFull = 5 };
 enum { kF32 = 0, kBF16 = 1 };
 
 // Prefill: query block of 128 rows per workgroup, key tiles of 64 rows.

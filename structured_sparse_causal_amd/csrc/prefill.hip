@@ -6,6 +6,8 @@
 // key ranges:
 //   window (pi-Attention section 2 item 1; LT2 section 2.1): [max(0,i-k), i]
 //   ECP (PAR block, ECP section 2):       [max(0,(floor(i/s)-1)*s), i]
+//   and the further masks (two-sided window, s-Split segments, ECP pair
+//   without the causal mask), each a range [key_lo(i), key_hi(i)].
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // every lane then owns ONE query and 32 keys of the tile, so the softmax row
 // max and sum are lane-local plus one exchange between the wave halves
@@ -155,11 +157,12 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
       }
   }
 
-  const int hi_wg = min(i0 + BM - 1, N - 1);
+  const int hi_i = key_hi(qi, N, p.mode, p.k_win, p.seg);
+  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
   const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
   const int ntiles = (hi_wg - t_begin) / BN + 1;
   const bool wave_live = q0 < N;
-  const int w_hi = min(q0 + 31, N - 1);
+  const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
   const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
   const float sl2 = p.scale_log2;
 
@@ -185,9 +188,9 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
 #pragma unroll
       for (int kk = 0; kk < D / 2; ++kk) s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk + h], qf[kk], s[kb], 0, 0, 0);
     }
-    // mask: key j visible to query i iff lo(i) <= j <= i (tile-local index of
-    // register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4)
-    const int a0 = lo_i - j0 - 4 * h, span = qi - lo_i;
+    // mask: key j visible to query i iff lo(i) <= j <= hi(i) (tile-local index
+    // of register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4)
+    const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -306,11 +309,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   }
 
   // ---- key-tile range ---------------------------------------------------
-  const int hi_wg = min(i0 + BM - 1, N - 1);
+  const int hi_i = key_hi(qi, N, p.mode, p.k_win, p.seg);
+  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
   const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
   const int ntiles = (hi_wg - t_begin) / BN + 1;
   const bool wave_live = q0 < N;
-  const int w_hi = min(q0 + 31, N - 1);
+  const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
+  const int w_hi_first = key_hi(min(q0, N - 1), N, p.mode, p.k_win, p.seg);   // smallest hi of the wave
   const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
   const int w_lo_last = key_lo(min(q0 + 31, N - 1), p.mode, p.k_win, p.seg);
   const bool w_allvalid = q0 + 31 < N;
@@ -386,11 +391,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
         }
       }
 
-      // ---- mask: key j visible to query i iff lo(i) <= j <= i -----------------
-      const bool full = w_allvalid && (j0 + BN - 1 <= q0) && (j0 >= w_lo_last);
+      // ---- mask: key j visible to query i iff lo(i) <= j <= hi(i) --------------
+      const bool full = w_allvalid && (j0 + BN - 1 <= w_hi_first) && (j0 >= w_lo_last);
       if (!full) {
         // tile-local index of register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4
-        const int a0 = lo_i - j0 - 4 * h, span = qi - lo_i;
+        const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

@@ -60,6 +60,18 @@ WORKLOADS = {
 }
 
 
+# The further mask modes at the workload scales above (forward measured in the
+# benchmark; seeds continue the numbering).
+MASK_WORKLOADS = {
+    "window_bidir_bf16": Workload("window_bidir_bf16", "window_bidir", "bf16", 1, 32, 32, 65536, 128,
+                                  k_win=1024, scale_inputs=True, seed=6),
+    "ssplit_bf16": Workload("ssplit_bf16", "ssplit", "bf16", 4, 12, 12, 4096, 64, seg=512,
+                            scale_inputs=True, seed=7),
+    "ecp_full_bf16": Workload("ecp_full_bf16", "ecp_full", "bf16", 4, 12, 12, 4096, 64, seg=512,
+                              scale_inputs=True, seed=8),
+}
+
+
 def _gen(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))

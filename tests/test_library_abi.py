@@ -61,7 +61,7 @@ def fwd(lib, q=Q, k=K, v=V, a=A, o=O, B=1, Hq=2, Hkv=2, N=256, d=64, dtype=BF16,
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(Hq=3, Hkv=2), INVALID),
-    (dict(mode=5), INVALID), (dict(k_win=-1), INVALID), (dict(M=-1), INVALID),
+    (dict(mode=9), INVALID), (dict(k_win=-1), INVALID), (dict(M=-1), INVALID),
     (dict(pi=0), INVALID), (dict(mode=ECP, seg=0), INVALID), (dict(q=None), INVALID),
     (dict(o=None), INVALID), (dict(a=None), INVALID), (dict(q=Q + 8), INVALID),
     (dict(a=A + 2), INVALID), (dict(o=Q), INVALID), (dict(o=K + 64), INVALID),
@@ -264,3 +264,24 @@ def test_decode_paged_workspace_size(lib):
         lib.sparse_attn_decode_workspace_size(64, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0)
     assert ws(1, 1, 1, 48, 4, 64, BF16, WINDOW, 8, 0, 0, 0) == 0           # page size not a power of two
     assert ws(1, 1, 1, 64, 4, 64, F32, WINDOW, 8, 0, 0, 0) == 0
+
+
+WINDOW_BIDIR, SSPLIT, ECP_FULL = 3, 4, 5
+
+
+def test_further_mask_modes_validation(lib):
+    # segment modes need seg >= 1; the two-sided window needs k_win >= 0
+    assert fwd(lib, mode=SSPLIT, seg=0) == INVALID
+    assert fwd(lib, mode=ECP_FULL, seg=0) == INVALID
+    assert fwd(lib, mode=WINDOW_BIDIR, k_win=-1) == INVALID
+    for m, kw in ((WINDOW_BIDIR, dict(k_win=8)), (SSPLIT, dict(seg=64)), (ECP_FULL, dict(seg=64))):
+        assert fwd(lib, mode=m, a=None, o=Q, **kw) == INVALID            # valid up to the overlap
+        assert b"overlaps" in lib.sparse_attn_last_error()
+        assert lib.sparse_attn_fwd_workspace_size(1, 2, 2, 256, 64, BF16, m, 8, 0, 0, 64) == 0
+    # a decoded token has no later keys: the two non-causal masks are prefill-only
+    assert dec(lib, mode=WINDOW_BIDIR) == UNSUPPORTED
+    assert dec(lib, mode=ECP_FULL, seg=64) == UNSUPPORTED
+    assert lib.sparse_attn_decode_workspace_size(2, 8, 2, 512, 128, BF16, WINDOW_BIDIR, 64, 0, 0, 0) == 0
+    # s-Split decodes: split plan over the seg rows of the query's segment
+    assert lib.sparse_attn_decode_workspace_size(2, 8, 2, 512, 128, BF16, SSPLIT, 0, 0, 0, 300) == \
+        256 * ((2 * 8 * 3 * 132 * 4 + 255) // 256)
