@@ -70,18 +70,19 @@ def _load():
             lib.orc_key_set.argtypes = [i64, i64, i32, i64, i64, i64, i64, vp, vp, i64]
             lib.orc_key_capacity.restype = i64
             lib.orc_key_capacity.argtypes = [i32, i64, i64, i64]
-            lib.orc_fwd_rows.restype = i32
-            lib.orc_fwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                         i32, i64, i64, i64, i64, vp, i64, vp]
-            lib.orc_decode.restype = i32
-            lib.orc_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                       i32, i64, i64, i64, i64, vp]
-            lib.orc_lse_rows.restype = i32
-            lib.orc_lse_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64,
-                                         i32, i64, i64, i64, i64, vp, i64, vp]
+            f64 = ctypes.c_double
+            lib.orc_fwd_rows_ex.restype = i32
+            lib.orc_fwd_rows_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                            i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, i64, vp]
+            lib.orc_decode_ex.restype = i32
+            lib.orc_decode_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          i32, i64, i64, i64, i64, f64, i32, vp, vp, vp]
+            lib.orc_lse_rows_ex.restype = i32
+            lib.orc_lse_rows_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64,
+                                            i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, i64, vp]
             lib.orc_bwd.restype = i32
             lib.orc_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                    i32, i64, i64, i64, i64, vp, vp, vp, vp]
+                                    i32, i64, i64, i64, i64, f64, vp, vp, vp, vp]
             lib.orc_num_threads.restype = i32
             lib.orc_set_num_threads.argtypes = [i32]
             _lib = lib
@@ -135,12 +136,39 @@ def key_set(i: int, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
     return keys[:n].copy(), labels[:n].copy()
 
 
+def _gate_args(gate_w, gate_b, Hq, d):
+    """Gate computed from the query: w [Hq, d], b [Hq] (fp32 inputs)."""
+    if gate_w is None:
+        return None, None
+    w32, b32 = _f32(gate_w), _f32(gate_b)
+    if w32.shape != (Hq, d) or b32.shape != (Hq,):
+        raise ValueError("oracle: gate_w must be [Hq, d] and gate_b [Hq]")
+    return w32, b32
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def _out_gate(out, out_gate):
+    """Output gate of the LT2 page (section 3): o * sigmoid(g), elementwise."""
+    if out_gate is None:
+        return out
+    g = _f32(out_gate).astype(np.float64)
+    return out * _sigmoid(g.reshape(out.shape) if g.size == out.size else g)
+
+
 def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
-        seg: int = 0, rows=None) -> np.ndarray:
+        seg: int = 0, rows=None, scale=None, cosine: bool = False, gate_w=None, gate_b=None,
+        out_gate=None) -> np.ndarray:
     """Forward attention in fp64.
 
     q [B,Hq,N,d], k/v [B,Hkv,N,d], alpha [B,Hq,N] (PI only).  With ``rows``
     (flat ids (b*Hq+h)*N+i) returns [len(rows), d]; otherwise [B,Hq,N,d].
+    Options: ``scale`` (default 1/sqrt(d)); ``cosine`` scores
+    scale * cos(q_i, k_j); ``gate_w`` [Hq,d] / ``gate_b`` [Hq]: alpha =
+    sigmoid(<w_h, q_i> + b_h) instead of the alpha input; ``out_gate``
+    (shaped like the output): o * sigmoid(out_gate).
     """
     lib = _load()
     q32, k32, v32 = _f32(q), _f32(k), _f32(v)
@@ -159,16 +187,22 @@ def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
         out = np.empty((sel.size, d), dtype=np.float64)
         sel_p, nsel = sel.ctypes.data, sel.size
-    rc = lib.orc_fwd_rows(q32.ctypes.data, k32.ctypes.data, v32.ctypes.data,
-                          a32.ctypes.data if a32 is not None else None,
-                          B, Hq, Hkv, N, d, m, int(k_win), int(pi), int(M), int(seg),
-                          sel_p, nsel, out.ctypes.data)
+    w32, b32 = _gate_args(gate_w, gate_b, Hq, d)
+    rc = lib.orc_fwd_rows_ex(q32.ctypes.data, k32.ctypes.data, v32.ctypes.data,
+                             a32.ctypes.data if a32 is not None else None,
+                             B, Hq, Hkv, N, d, m, int(k_win), int(pi), int(M), int(seg),
+                             1.0 / np.sqrt(d) if scale is None else float(scale), int(bool(cosine)),
+                             w32.ctypes.data if w32 is not None else None,
+                             b32.ctypes.data if b32 is not None else None,
+                             sel_p, nsel, out.ctypes.data)
     _check(rc)
-    return out
+    if out_gate is not None and rows is not None:
+        out_gate = _f32(out_gate).reshape(-1, d)[np.asarray(rows, dtype=np.int64).ravel()]
+    return _out_gate(out, out_gate)
 
 
 def lse(q, k, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
-        rows=None) -> np.ndarray:
+        rows=None, scale=None, cosine: bool = False, gate_w=None, gate_b=None) -> np.ndarray:
     """Log-sum-exp of each row's scores (natural log), fp64: [B,Hq,N], or
     [len(rows)] for flat row ids."""
     lib = _load()
@@ -185,23 +219,39 @@ def lse(q, k, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg:
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
         out = np.empty(sel.size, dtype=np.float64)
         sel_p, nsel = sel.ctypes.data, sel.size
-    rc = lib.orc_lse_rows(q32.ctypes.data, k32.ctypes.data,
-                          a32.ctypes.data if a32 is not None else None,
-                          B, Hq, Hkv, N, d, _mode(mode), int(k_win), int(pi), int(M), int(seg),
-                          sel_p, nsel, out.ctypes.data)
+    w32, b32 = _gate_args(gate_w, gate_b, Hq, d)
+    rc = lib.orc_lse_rows_ex(q32.ctypes.data, k32.ctypes.data,
+                             a32.ctypes.data if a32 is not None else None,
+                             B, Hq, Hkv, N, d, _mode(mode), int(k_win), int(pi), int(M), int(seg),
+                             1.0 / np.sqrt(d) if scale is None else float(scale), int(bool(cosine)),
+                             w32.ctypes.data if w32 is not None else None,
+                             b32.ctypes.data if b32 is not None else None,
+                             sel_p, nsel, out.ctypes.data)
     _check(rc)
     return out
 
 
-def bwd(q, k, v, alpha, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0):
+def bwd(q, k, v, alpha, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
+        scale=None, out_gate=None):
     """Backward pass in fp64 (the chain rule through the forward definition;
     the gate gradient follows pi-Attention section 2 item 3).
-    Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d], dalpha [B,Hq,N] or None)."""
+    Returns (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d], dalpha [B,Hq,N] or None).
+    With ``out_gate`` g (output y = o * sigmoid(g), LT2 section 3), dO is the
+    gradient of y: the attention's output gradient is dO * sigmoid(g), and a
+    fifth result dg = dO * o * sigmoid(g) * (1 - sigmoid(g)) is returned."""
     lib = _load()
-    q32, k32, v32, do32 = _f32(q), _f32(k), _f32(v), _f32(dO)
+    q32, k32, v32 = _f32(q), _f32(k), _f32(v)
+    do64 = _f32(dO).astype(np.float64)
+    dg = None
+    if out_gate is not None:
+        sg = _sigmoid(_f32(out_gate))
+        o = fwd(q, k, v, alpha, mode=mode, k_win=k_win, pi=pi, M=M, seg=seg, scale=scale)
+        dg = do64 * o * sg * (1.0 - sg)
+        do64 = do64 * sg
+    do64 = np.ascontiguousarray(do64)
     B, Hq, N, d = q32.shape
     Hkv = k32.shape[1]
-    if k32.shape != (B, Hkv, N, d) or v32.shape != k32.shape or do32.shape != q32.shape:
+    if k32.shape != (B, Hkv, N, d) or v32.shape != k32.shape or do64.shape != q32.shape:
         raise ValueError("oracle: shape mismatch")
     m = _mode(mode)
     a32 = _f32(alpha) if alpha is not None else None
@@ -210,16 +260,20 @@ def bwd(q, k, v, alpha, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, se
     dv = np.empty((B, Hkv, N, d), dtype=np.float64)
     da = np.zeros((B, Hq, N), dtype=np.float64) if m == MODES["pi"] else None
     rc = lib.orc_bwd(q32.ctypes.data, k32.ctypes.data, v32.ctypes.data,
-                     a32.ctypes.data if a32 is not None else None, do32.ctypes.data,
+                     a32.ctypes.data if a32 is not None else None, do64.ctypes.data,
                      B, Hq, Hkv, N, d, m, int(k_win), int(pi), int(M), int(seg),
+                     1.0 / np.sqrt(d) if scale is None else float(scale),
                      dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
                      da.ctypes.data if da is not None else None)
     _check(rc)
+    if dg is not None:
+        return dq, dk, dv, da, dg
     return dq, dk, dv, da
 
 
 def decode(q, k_cache, v_cache, lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
-           M: int = 0, seg: int = 0) -> np.ndarray:
+           M: int = 0, seg: int = 0, scale=None, cosine: bool = False, gate_w=None, gate_b=None,
+           out_gate=None) -> np.ndarray:
     """Single-token decode in fp64: the query of sequence b is at position
     lens[b]-1 and attends that position's key set inside the cache.
     q [B,Hq,d], caches [B,Hkv,Lmax,d], lens [B], alpha [B,Hq] -> [B,Hq,d]."""
@@ -234,12 +288,15 @@ def decode(q, k_cache, v_cache, lens, alpha=None, *, mode, k_win: int = 0, pi: i
     ln = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
     a32 = _f32(alpha) if alpha is not None else None
     out = np.empty((B, Hq, d), dtype=np.float64)
-    rc = lib.orc_decode(q32.ctypes.data, kc.ctypes.data, vc.ctypes.data, ln.ctypes.data,
-                        a32.ctypes.data if a32 is not None else None,
-                        B, Hq, Hkv, Lmax, d, _mode(mode), int(k_win), int(pi), int(M),
-                        int(seg), out.ctypes.data)
+    w32, b32 = _gate_args(gate_w, gate_b, Hq, d)
+    rc = lib.orc_decode_ex(q32.ctypes.data, kc.ctypes.data, vc.ctypes.data, ln.ctypes.data,
+                           a32.ctypes.data if a32 is not None else None,
+                           B, Hq, Hkv, Lmax, d, _mode(mode), int(k_win), int(pi), int(M),
+                           int(seg), 1.0 / np.sqrt(d) if scale is None else float(scale),
+                           int(bool(cosine)), w32.ctypes.data if w32 is not None else None,
+                           b32.ctypes.data if b32 is not None else None, out.ctypes.data)
     _check(rc)
-    return out
+    return _out_gate(out, out_gate)
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

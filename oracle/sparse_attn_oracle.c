@@ -38,6 +38,17 @@
  *         half-segment c see all of half-segments c-1 and c).
  *
  *   score(i, j) = <q_i, k_j> / sqrt(d) + prior(i, j)
+ *
+ * Options of the *_ex entry points (the fused gate and epilogue variants):
+ *   - a score scale other than 1/sqrt(d);
+ *   - scaled cosine scores (the attention branch of the hybrid
+ *     GSS-Transformer page, methodology item 1):
+ *       score(i, j) = scale * <q_i, k_j> / (|q_i| |k_j|) + prior(i, j);
+ *   - the gate computed from the query (pi-Attention section 2 item 3: a
+ *     light per-token, per-head network produces alpha), read as one linear
+ *     layer per head on the query: alpha_i = sigmoid(<w_h, q_i> + b_h).
+ *   The output gate o * sigmoid(g) of the LT2 page (section 3) is elementwise
+ *   on the output and applied by the Python wrapper.
  *   o_i        = sum_j exp(score(i,j) - max) v_j / sum_j exp(score(i,j) - max)
  *
  * Everything is evaluated in double precision with libm exp/log.  Inputs are
@@ -139,19 +150,30 @@ int64_t orc_key_set(int64_t i, int64_t N, int mode, int64_t k_win, int64_t pi, i
  * 0 of the key/value head (row stride d).  log_local/log_skip are the priors
  * (0 for modes without a gate).  Writes d doubles to out.
  */
+/* <q, k>, or the cosine <q, k> / (|q| |k|) when cosine is set. */
+static double orc_dot(const float *qrow, const float *krow, int64_t d, int cosine)
+{
+    double dot = 0.0, qq = 0.0, kk = 0.0;
+    int64_t c;
+    for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)krow[c];
+    if (!cosine) return dot;
+    for (c = 0; c < d; ++c) {
+        qq += (double)qrow[c] * (double)qrow[c];
+        kk += (double)krow[c] * (double)krow[c];
+    }
+    return dot / (sqrt(qq) * sqrt(kk));
+}
+
 static void orc_row(const float *qrow, const float *kmat, const float *vmat,
-                    int64_t d, double log_local, double log_skip,
+                    int64_t d, double scale, int cosine, double log_local, double log_skip,
                     const int64_t *keys, const int32_t *labels, int64_t n,
                     double *score, double *out)
 {
-    const double inv_sqrt_d = 1.0 / sqrt((double)d);
     double mx = -INFINITY, denom = 0.0;
     int64_t t, c;
     for (t = 0; t < n; ++t) {
         const float *krow = kmat + keys[t] * d;
-        double dot = 0.0;
-        for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)krow[c];
-        score[t] = dot * inv_sqrt_d + (labels[t] == ORC_LOCAL ? log_local : log_skip);
+        score[t] = orc_dot(qrow, krow, d, cosine) * scale + (labels[t] == ORC_LOCAL ? log_local : log_skip);
         if (score[t] > mx) mx = score[t];
     }
     for (c = 0; c < d; ++c) out[c] = 0.0;
@@ -177,19 +199,36 @@ static int orc_check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int m
 }
 
 /* Priors of one row.  alpha must lie in (0, 1]; alpha = 1 makes the skip
-   prior log(0) = -inf, which removes the skip keys from the softmax. */
-static int orc_priors(int mode, const float *alpha, int64_t at, double *lp, double *ls)
+   prior log(0) = -inf, which removes the skip keys from the softmax.  With a
+   gate (w_h: d weights, b_h: bias) alpha comes from the query row instead:
+   alpha = sigmoid(<w_h, q_i> + b_h). */
+static int orc_priors_q(int mode, const float *alpha, int64_t at, const float *qrow, const float *w_h,
+                        const float *b_h, int64_t d, double *lp, double *ls)
 {
     double a;
+    int64_t c;
     *lp = 0.0;
     *ls = 0.0;
     if (mode != ORC_MODE_PI) return ORC_OK;
+    if (w_h != NULL) {
+        double z = (double)*b_h;
+        for (c = 0; c < d; ++c) z += (double)w_h[c] * (double)qrow[c];
+        a = 1.0 / (1.0 + exp(-z));
+        *lp = log(a);
+        *ls = log(1.0 - a);
+        return ORC_OK;
+    }
     if (alpha == NULL) return ORC_ERR_ALPHA;
     a = (double)alpha[at];
     if (!(a > 0.0 && a <= 1.0)) return ORC_ERR_ALPHA;
     *lp = log(a);
     *ls = log(1.0 - a); /* -inf at a == 1 */
     return ORC_OK;
+}
+
+static int orc_priors(int mode, const float *alpha, int64_t at, double *lp, double *ls)
+{
+    return orc_priors_q(mode, alpha, at, NULL, NULL, NULL, 0, lp, ls);
 }
 
 /*
@@ -200,10 +239,11 @@ static int orc_priors(int mode, const float *alpha, int64_t at, double *lp, doub
  *   out   [nsel, d] doubles (or [B, Hq, N, d] when sel is NULL)
  * Returns ORC_OK or a negative error code.
  */
-int orc_fwd_rows(const float *q, const float *k, const float *v, const float *alpha,
-                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                 int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
-                 const int64_t *sel, int64_t nsel, double *out)
+int orc_fwd_rows_ex(const float *q, const float *k, const float *v, const float *alpha,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                    double scale, int cosine, const float *gate_w, const float *gate_b,
+                    const int64_t *sel, int64_t nsel, double *out)
 {
     int64_t cap, total, r;
     int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
@@ -228,11 +268,12 @@ int orc_fwd_rows(const float *q, const float *k, const float *v, const float *al
             h = (row / N) % Hq;
             b = row / (N * Hq);
             g = h / (Hq / Hkv);
-            if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) continue;
+            if ((local_err = orc_priors_q(mode, alpha, row, q + row * d, gate_w ? gate_w + h * d : NULL,
+                                          gate_b ? gate_b + h : NULL, d, &lp, &ls)) != ORC_OK) continue;
             n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             orc_row(q + row * d, k + (b * Hkv + g) * N * d, v + (b * Hkv + g) * N * d,
-                    d, lp, ls, keys, labels, n, score, out + r * d);
+                    d, scale, cosine, lp, ls, keys, labels, n, score, out + r * d);
         }
         if (local_err != ORC_OK) {
 #pragma omp critical
@@ -245,6 +286,15 @@ int orc_fwd_rows(const float *q, const float *k, const float *v, const float *al
     return err;
 }
 
+int orc_fwd_rows(const float *q, const float *k, const float *v, const float *alpha,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                 const int64_t *sel, int64_t nsel, double *out)
+{
+    return orc_fwd_rows_ex(q, k, v, alpha, B, Hq, Hkv, N, d, mode, k_win, pi, M, seg,
+                           1.0 / sqrt((double)d), 0, NULL, NULL, sel, nsel, out);
+}
+
 /*
  * Single-token decode over a KV cache: for every sequence b and query head h
  * the query sits at position i = lens[b] - 1 and attends the key set of i,
@@ -253,10 +303,10 @@ int orc_fwd_rows(const float *q, const float *k, const float *v, const float *al
  *   q     [B, Hq, d]          kc, vc [B, Hkv, Lmax, d]     lens [B] int32
  *   alpha [B, Hq] (PI only)   out    [B, Hq, d] doubles
  */
-int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *lens,
-               const float *alpha, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax,
-               int64_t d, int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
-               double *out)
+int orc_decode_ex(const float *q, const float *kc, const float *vc, const int32_t *lens,
+                  const float *alpha, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax,
+                  int64_t d, int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                  double scale, int cosine, const float *gate_w, const float *gate_b, double *out)
 {
     int64_t cap, r;
     int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
@@ -278,11 +328,12 @@ int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *
             int64_t b = r / Hq, h = r % Hq, g = h / (Hq / Hkv), i = lens[b] - 1, n;
             double lp, ls;
             if (local_err != ORC_OK) continue;
-            if ((local_err = orc_priors(mode, alpha, r, &lp, &ls)) != ORC_OK) continue;
+            if ((local_err = orc_priors_q(mode, alpha, r, q + r * d, gate_w ? gate_w + h * d : NULL,
+                                          gate_b ? gate_b + h : NULL, d, &lp, &ls)) != ORC_OK) continue;
             n = orc_key_set(i, i + 1, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             orc_row(q + r * d, kc + (b * Hkv + g) * Lmax * d, vc + (b * Hkv + g) * Lmax * d,
-                    d, lp, ls, keys, labels, n, score, out + r * d);
+                    d, scale, cosine, lp, ls, keys, labels, n, score, out + r * d);
         }
         if (local_err != ORC_OK) {
 #pragma omp critical
@@ -295,16 +346,26 @@ int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *
     return err;
 }
 
+int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *lens,
+               const float *alpha, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax,
+               int64_t d, int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+               double *out)
+{
+    return orc_decode_ex(q, kc, vc, lens, alpha, B, Hq, Hkv, Lmax, d, mode, k_win, pi, M, seg,
+                         1.0 / sqrt((double)d), 0, NULL, NULL, out);
+}
+
 /*
  * Log-sum-exp of the scores of selected rows (natural log units): the
  * softmax normaliser a training forward keeps for the backward pass,
  *   lse_i = log sum_{j in K(i)} exp(score(i, j)).
  *   sel/nsel as for orc_fwd_rows; out[nsel] doubles.
  */
-int orc_lse_rows(const float *q, const float *k, const float *alpha,
-                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                 int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
-                 const int64_t *sel, int64_t nsel, double *out)
+int orc_lse_rows_ex(const float *q, const float *k, const float *alpha,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                    double scale, int cosine, const float *gate_w, const float *gate_b,
+                    const int64_t *sel, int64_t nsel, double *out)
 {
     int64_t cap, total, r;
     int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
@@ -318,10 +379,9 @@ int orc_lse_rows(const float *q, const float *k, const float *alpha,
         int64_t *keys = (int64_t *)malloc((size_t)cap * sizeof(int64_t));
         int32_t *labels = (int32_t *)malloc((size_t)cap * sizeof(int32_t));
         int local_err = (keys && labels) ? ORC_OK : ORC_ERR_NOMEM;
-        const double inv_sqrt_d = 1.0 / sqrt((double)d);
 #pragma omp for schedule(dynamic, 64)
         for (r = 0; r < nsel; ++r) {
-            int64_t row = sel ? sel[r] : r, b, h, i, g, n, t, c;
+            int64_t row = sel ? sel[r] : r, b, h, i, g, n, t;
             double lp, ls, mx = -INFINITY, sum = 0.0;
             const float *qrow, *kmat;
             if (local_err != ORC_OK) continue;
@@ -330,22 +390,20 @@ int orc_lse_rows(const float *q, const float *k, const float *alpha,
             h = (row / N) % Hq;
             b = row / (N * Hq);
             g = h / (Hq / Hkv);
-            if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) continue;
+            if ((local_err = orc_priors_q(mode, alpha, row, q + row * d, gate_w ? gate_w + h * d : NULL,
+                                          gate_b ? gate_b + h : NULL, d, &lp, &ls)) != ORC_OK) continue;
             n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             qrow = q + row * d;
             kmat = k + (b * Hkv + g) * N * d;
             for (t = 0; t < n; ++t) {
-                double dot = 0.0, sc;
-                for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)kmat[keys[t] * d + c];
-                sc = dot * inv_sqrt_d + (labels[t] == ORC_LOCAL ? lp : ls);
+                const double sc = orc_dot(qrow, kmat + keys[t] * d, d, cosine) * scale +
+                                  (labels[t] == ORC_LOCAL ? lp : ls);
                 if (sc > mx) mx = sc;
             }
-            for (t = 0; t < n; ++t) {
-                double dot = 0.0;
-                for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)kmat[keys[t] * d + c];
-                sum += exp(dot * inv_sqrt_d + (labels[t] == ORC_LOCAL ? lp : ls) - mx);
-            }
+            for (t = 0; t < n; ++t)
+                sum += exp(orc_dot(qrow, kmat + keys[t] * d, d, cosine) * scale +
+                           (labels[t] == ORC_LOCAL ? lp : ls) - mx);
             out[r] = mx + log(sum);
         }
         if (local_err != ORC_OK) {
@@ -356,6 +414,15 @@ int orc_lse_rows(const float *q, const float *k, const float *alpha,
         free(labels);
     }
     return err;
+}
+
+int orc_lse_rows(const float *q, const float *k, const float *alpha,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+                 const int64_t *sel, int64_t nsel, double *out)
+{
+    return orc_lse_rows_ex(q, k, alpha, B, Hq, Hkv, N, d, mode, k_win, pi, M, seg,
+                           1.0 / sqrt((double)d), 0, NULL, NULL, sel, nsel, out);
 }
 
 /*
@@ -373,14 +440,16 @@ int orc_lse_rows(const float *q, const float *k, const float *alpha,
  * pi-Attention section 2 item 3).  The skip term is formed as
  * exp(score without prior - lse_i) (dP_ij - D_i), which equals
  * dS_ij / (1 - alpha_i) and stays finite at alpha = 1.
- *   dO [B, Hq, N, d] fp32;  dq [B, Hq, N, d], dk, dv [B, Hkv, N, d] doubles;
+ * scale is the score scale (1/sqrt(d) for the method as defined; the
+ * formulas above use it in place of 1/sqrt(d)).
+ *   dO [B, Hq, N, d] doubles;  dq [B, Hq, N, d], dk, dv [B, Hkv, N, d] doubles;
  *   dalpha [B, Hq, N] doubles or NULL (PI only).
  * Work is split over (batch, KV head): one thread owns the dk/dv rows of a
  * KV head and every query row of its group.
  */
-int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, const float *dO,
+int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, const double *dO,
             int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-            int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
+            int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg, double scale,
             double *dq, double *dk, double *dv, double *dalpha)
 {
     int64_t cap, u;
@@ -396,7 +465,6 @@ int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, 
         double *pr = (double *)malloc((size_t)cap * sizeof(double));
         double *dp = (double *)malloc((size_t)cap * sizeof(double));
         int local_err = (keys && labels && sc && pr && dp) ? ORC_OK : ORC_ERR_NOMEM;
-        const double inv_sqrt_d = 1.0 / sqrt((double)d);
 #pragma omp for schedule(dynamic, 1)
         for (u = 0; u < B * Hkv; ++u) {
             const int64_t b = u / Hkv, g = u % Hkv, grp = Hq / Hkv;
@@ -409,7 +477,8 @@ int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, 
                 const int64_t h = g * grp + hh;
                 for (i = 0; i < N; ++i) {
                     const int64_t row = (b * Hq + h) * N + i;
-                    const float *qrow = q + row * d, *dorow = dO + row * d;
+                    const float *qrow = q + row * d;
+                    const double *dorow = dO + row * d;
                     double lp, ls, mx = -INFINITY, sum = 0.0, lse, D = 0.0, da = 0.0;
                     if ((local_err = orc_priors(mode, alpha, row, &lp, &ls)) != ORC_OK) break;
                     n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
@@ -417,7 +486,7 @@ int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, 
                     for (t = 0; t < n; ++t) {
                         double dot = 0.0;
                         for (c = 0; c < d; ++c) dot += (double)qrow[c] * (double)kmat[keys[t] * d + c];
-                        sc[t] = dot * inv_sqrt_d;   /* without prior */
+                        sc[t] = dot * scale;   /* without prior */
                         {
                             const double full = sc[t] + (labels[t] == ORC_LOCAL ? lp : ls);
                             if (full > mx) mx = full;
@@ -428,7 +497,7 @@ int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, 
                     for (t = 0; t < n; ++t) {
                         double dot = 0.0;
                         pr[t] = exp(sc[t] + (labels[t] == ORC_LOCAL ? lp : ls) - lse);
-                        for (c = 0; c < d; ++c) dot += (double)dorow[c] * (double)vmat[keys[t] * d + c];
+                        for (c = 0; c < d; ++c) dot += dorow[c] * (double)vmat[keys[t] * d + c];
                         dp[t] = dot;
                         D += pr[t] * dot;
                     }
@@ -437,9 +506,9 @@ int orc_bwd(const float *q, const float *k, const float *v, const float *alpha, 
                         const double ds = pr[t] * (dp[t] - D);
                         const int64_t j = keys[t];
                         for (c = 0; c < d; ++c) {
-                            dq[row * d + c] += ds * (double)kmat[j * d + c] * inv_sqrt_d;
-                            dkm[j * d + c] += ds * (double)qrow[c] * inv_sqrt_d;
-                            dvm[j * d + c] += pr[t] * (double)dorow[c];
+                            dq[row * d + c] += ds * (double)kmat[j * d + c] * scale;
+                            dkm[j * d + c] += ds * (double)qrow[c] * scale;
+                            dvm[j * d + c] += pr[t] * dorow[c];
                         }
                         if (mode == ORC_MODE_PI) {
                             if (labels[t] == ORC_LOCAL) da += ds / (double)alpha[row];
