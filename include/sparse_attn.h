@@ -229,6 +229,75 @@ int sparse_attn_decode_paged(const void *q, const void *k_pages, const void *v_p
                              int max_pages, int d, int dtype, int mode, int k_win, int pi, int M,
                              int seg, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Fused gate and epilogue options (the *_ex entry points).  A NULL options
+ * pointer, or a zero-initialised struct, means the plain operation.
+ *   score_scale  > 0: scores use this scale instead of 1/sqrt(d).
+ *   cosine       nonzero: scaled cosine scores, score_scale * cos(q_i, k_j)
+ *                (the attention branch of the hybrid GSS-Transformer page,
+ *                methodology item 1); q and k rows must be nonzero.  The
+ *                forward keeps an L2-normalised copy of k in the workspace.
+ *   gate_w, gate_b  PI mode: the gate is computed in-kernel from the query,
+ *                alpha_i = sigmoid(<gate_w[h], q_i> + gate_b[h]) (pi-Attention
+ *                section 2 item 3: a light per-token, per-head network; read
+ *                here as one linear layer per head on the query), and the
+ *                alpha argument is ignored.  gate_w fp32 [Hq, d], gate_b fp32
+ *                [Hq], device memory, 4-byte aligned; both or neither.
+ *   out_gate     output gate of the LT2 page (section 3): the result is
+ *                o * sigmoid(out_gate), out_gate shaped and typed like o
+ *                (decode: [B, Hq, d]), device memory, 16-byte aligned.
+ */
+typedef struct sa_options {
+  float score_scale;
+  int cosine;
+  const float *gate_w;
+  const float *gate_b;
+  const void *out_gate;
+} sa_options;
+
+/*
+ * sparse_attn_fwd / sparse_attn_fwd_lse with options (lse may be NULL).
+ * Workspace: sparse_attn_fwd_ex_workspace_size (cosine adds B*Hkv*N*d
+ * elements for the normalised keys).  Errors as sparse_attn_fwd, plus
+ * SA_ERR_INVALID for a bad option (negative or non-finite score_scale, only
+ * one of gate_w / gate_b, the gate outside PI mode, misalignment, out_gate
+ * overlapping o).
+ */
+size_t sparse_attn_fwd_ex_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype,
+                                         int mode, int k_win, int pi, int M, int seg,
+                                         const sa_options *opt);
+int sparse_attn_fwd_ex(const void *q, const void *k, const void *v, const float *alpha, void *o,
+                       float *lse, int B, int Hq, int Hkv, int N, int d, int dtype,
+                       int mode, int k_win, int pi, int M, int seg, const sa_options *opt,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sparse_attn_decode (contiguous caches) with options; bf16 I/O only
+ * (SA_ERR_UNSUPPORTED otherwise).  Workspace as sparse_attn_decode.
+ */
+int sparse_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                          const int *cache_lens, const float *alpha, void *o,
+                          int B, int Hq, int Hkv, int Lmax, int d, int dtype,
+                          int mode, int k_win, int pi, int M, int seg, const sa_options *opt,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sparse_attn_bwd with options: score_scale and out_gate (cosine and the
+ * query-driven gate return SA_ERR_UNSUPPORTED).  With out_gate, o is the
+ * gated output y = o_attn * sigmoid(g) of sparse_attn_fwd_ex, dO is dL/dy,
+ * and dgate [B, Hq, N, d] bf16 receives dL/dg = dO * y * (1 - sigmoid(g));
+ * the workspace (sparse_attn_bwd_ex_workspace_size) adds B*Hq*N*d bf16.
+ */
+size_t sparse_attn_bwd_ex_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype,
+                                         int mode, int k_win, int pi, int M, int seg,
+                                         const sa_options *opt);
+int sparse_attn_bwd_ex(const void *q, const void *k, const void *v, const float *alpha,
+                       const void *o, const float *lse, const void *dO,
+                       void *dq, void *dk, void *dv, float *dalpha,
+                       int B, int Hq, int Hkv, int N, int d, int dtype,
+                       int mode, int k_win, int pi, int M, int seg, const sa_options *opt,
+                       void *dgate, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *sparse_attn_status_string(int status);
 

@@ -28,6 +28,27 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
 SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 
+
+
+class SaOptions(ctypes.Structure):
+    """struct sa_options of the C ABI (fused gate and epilogue options)."""
+    _fields_ = [("score_scale", ctypes.c_float), ("cosine", ctypes.c_int),
+                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p), ("out_gate", ctypes.c_void_p)]
+
+
+def _options(score_scale=0.0, cosine=False, gate_w=None, gate_b=None, out_gate=None):
+    """SaOptions for the given keywords, or None when all are off."""
+    if not score_scale and not cosine and gate_w is None and gate_b is None and out_gate is None:
+        return None
+    for t, name in ((gate_w, "gate_w"), (gate_b, "gate_b")):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("%s must be fp32" % name)
+    return SaOptions(float(score_scale), int(bool(cosine)),
+                     None if gate_w is None else gate_w.data_ptr(),
+                     None if gate_b is None else gate_b.data_ptr(),
+                     None if out_gate is None else out_gate.data_ptr())
+
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 _lock = threading.Lock()
@@ -38,6 +59,8 @@ EXPORTED = ("sparse_attn_fwd_workspace_size", "sparse_attn_fwd", "sparse_attn_fw
             "sparse_attn_decode_workspace_size", "sparse_attn_decode",
             "sparse_attn_decode_ring_workspace_size", "sparse_attn_decode_ring",
             "sparse_attn_decode_paged_workspace_size", "sparse_attn_decode_paged",
+            "sparse_attn_fwd_ex_workspace_size", "sparse_attn_fwd_ex", "sparse_attn_decode_ex",
+            "sparse_attn_bwd_ex_workspace_size", "sparse_attn_bwd_ex",
             "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_version")
 
 
@@ -78,6 +101,17 @@ def load_library():
         lib.sparse_attn_decode_paged_workspace_size.argtypes = [i] * 12
         lib.sparse_attn_decode_paged.restype = i
         lib.sparse_attn_decode_paged.argtypes = [vp] * 7 + [i] * 13 + [vp, sz, vp]
+        op = ctypes.POINTER(SaOptions)
+        lib.sparse_attn_fwd_ex_workspace_size.restype = sz
+        lib.sparse_attn_fwd_ex_workspace_size.argtypes = [i] * 11 + [op]
+        lib.sparse_attn_fwd_ex.restype = i
+        lib.sparse_attn_fwd_ex.argtypes = [vp] * 6 + [i] * 11 + [op, vp, sz, vp]
+        lib.sparse_attn_decode_ex.restype = i
+        lib.sparse_attn_decode_ex.argtypes = [vp] * 6 + [i] * 11 + [op, vp, sz, vp]
+        lib.sparse_attn_bwd_ex_workspace_size.restype = sz
+        lib.sparse_attn_bwd_ex_workspace_size.argtypes = [i] * 11 + [op]
+        lib.sparse_attn_bwd_ex.restype = i
+        lib.sparse_attn_bwd_ex.argtypes = [vp] * 11 + [i] * 11 + [op, vp, vp, sz, vp]
         lib.sparse_attn_decode_workspace_size.restype = sz
         lib.sparse_attn_decode_workspace_size.argtypes = [i] * 11
         lib.sparse_attn_decode.restype = i
@@ -149,13 +183,16 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
-        out=None, workspace=None, lse=None):
+        out=None, workspace=None, lse=None, score_scale: float = 0.0, cosine: bool = False,
+        gate_w=None, gate_b=None, out_gate=None):
     """Prefill forward: q [B,Hq,N,d], k/v [B,Hkv,N,d] (bf16 or fp32, on the
     GPU), alpha [B,Hq,N] fp32 for the gated mode.  Returns o [B,Hq,N,d].
     With ``lse`` (an fp32 [B,Hq,N] tensor) the row log-sum-exp is written
-    too (the training forward)."""
+    too (the training forward).  Options (sa_options): score_scale, cosine,
+    gate_w [Hq,d] / gate_b [Hq] (alpha from the query), out_gate (like o)."""
     lib = load_library()
-    _need_gpu(q, k, v, alpha, out, workspace)
+    _need_gpu(q, k, v, alpha, out, workspace, gate_w, gate_b, out_gate)
+    opt = _options(score_scale, cosine, gate_w, gate_b, out_gate)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-d [B, H, N, d]")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -174,6 +211,23 @@ def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, s
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
     dt = _DTYPES[q.dtype]
+    if opt is not None:
+        if out_gate is not None and (out_gate.shape != q.shape or out_gate.dtype != q.dtype):
+            raise ValueError("out_gate must match o")
+        if lse is not None:
+            _need_gpu(lse)
+            if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+                raise ValueError("lse must be fp32 [B, Hq, N]")
+        nbytes = int(lib.sparse_attn_fwd_ex_workspace_size(B, Hq, Hkv, N, d, dt, m, k_win, pi, M, seg,
+                                                           ctypes.byref(opt)))
+        ws = _workspace(nbytes, q.device, workspace)
+        rc = lib.sparse_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(out), _ptr(lse),
+                                    B, Hq, Hkv, N, d, dt, m, int(k_win), int(pi), int(M), int(seg),
+                                    ctypes.byref(opt), _ptr(ws), nbytes if ws is not None else 0,
+                                    _stream(q.device))
+        if rc != SA_OK:
+            _raise(lib, rc, "sparse_attn_fwd_ex")
+        return out
     nbytes = int(lib.sparse_attn_fwd_workspace_size(B, Hq, Hkv, N, d, dt, m, k_win, pi, M, seg))
     ws = _workspace(nbytes, q.device, workspace)
     if lse is None:
@@ -199,12 +253,14 @@ def bwd_workspace_size(B, Hq, Hkv, N, d, dtype, mode, k_win=0, pi=0, M=0, seg=0)
 
 
 def bwd(q, k, v, alpha, o, lse, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
-        seg: int = 0, workspace=None):
+        seg: int = 0, workspace=None, score_scale: float = 0.0, out_gate=None):
     """Backward pass (bf16): gradients given dO for the forward that produced
     o and lse (``fwd(..., lse=...)``).  Returns (dq, dk, dv, dalpha); dalpha
-    is an fp32 [B,Hq,N] tensor for the gated mode with alpha, else None."""
+    is an fp32 [B,Hq,N] tensor for the gated mode with alpha, else None.
+    With ``out_gate`` (o is then the gated output) a fifth result dgate."""
     lib = load_library()
-    _need_gpu(q, k, v, alpha, o, lse, dO, workspace)
+    _need_gpu(q, k, v, alpha, o, lse, dO, workspace, out_gate)
+    opt = _options(score_scale, False, None, None, out_gate)
     if q.dtype != torch.bfloat16 or any(t.dtype != torch.bfloat16 for t in (k, v, o, dO)):
         raise NotImplementedError("the backward pass takes bf16 q, k, v, o, dO")
     B, Hq, N, d = q.shape
@@ -216,6 +272,18 @@ def bwd(q, k, v, alpha, o, lse, dO, *, mode, k_win: int = 0, pi: int = 0, M: int
     m = _mode(mode)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dalpha = torch.empty_like(alpha) if (alpha is not None and m == MODE_PI) else None
+    if opt is not None:
+        dgate = torch.empty_like(o) if out_gate is not None else None
+        nbytes = int(lib.sparse_attn_bwd_ex_workspace_size(B, Hq, Hkv, N, d, DTYPE_BF16, m, k_win, pi, M, seg,
+                                                           ctypes.byref(opt)))
+        ws = _workspace(nbytes, q.device, workspace)
+        rc = lib.sparse_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha),
+                                    B, Hq, Hkv, N, d, DTYPE_BF16, m, int(k_win), int(pi), int(M), int(seg),
+                                    ctypes.byref(opt), _ptr(dgate), _ptr(ws), nbytes, _stream(q.device))
+        if rc != SA_OK:
+            _raise(lib, rc, "sparse_attn_bwd_ex")
+        return (dq, dk, dv, dalpha, dgate) if out_gate is not None else (dq, dk, dv, dalpha)
     nbytes = int(lib.sparse_attn_bwd_workspace_size(B, Hq, Hkv, N, d, DTYPE_BF16, m, k_win, pi, M, seg))
     ws = _workspace(nbytes, q.device, workspace)
     rc = lib.sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO),
@@ -228,11 +296,14 @@ def bwd(q, k, v, alpha, o, lse, dO, *, mode, k_win: int = 0, pi: int = 0, M: int
 
 
 def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
-           M: int = 0, seg: int = 0, out=None, workspace=None):
+           M: int = 0, seg: int = 0, out=None, workspace=None, score_scale: float = 0.0,
+           cosine: bool = False, gate_w=None, gate_b=None, out_gate=None):
     """Single-token decode: q [B,Hq,d], caches [B,Hkv,Lmax,d], cache_lens [B]
-    int32 on the GPU, alpha [B,Hq] fp32 for the gated mode.  Returns o [B,Hq,d]."""
+    int32 on the GPU, alpha [B,Hq] fp32 for the gated mode.  Returns o [B,Hq,d].
+    Options as for ``fwd`` (bf16 only); out_gate is [B,Hq,d]."""
     lib = load_library()
-    _need_gpu(q, k_cache, v_cache, cache_lens, alpha, out, workspace)
+    _need_gpu(q, k_cache, v_cache, cache_lens, alpha, out, workspace, gate_w, gate_b, out_gate)
+    opt = _options(score_scale, cosine, gate_w, gate_b, out_gate)
     if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, d] and caches [B, Hkv, Lmax, d]")
     if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
@@ -252,6 +323,16 @@ def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0,
     nbytes = int(lib.sparse_attn_decode_workspace_size(B, Hq, Hkv, Lmax, d, dt, m, k_win, pi,
                                                        M, seg))
     ws = _workspace(nbytes, q.device, workspace)
+    if opt is not None:
+        if out_gate is not None and (out_gate.shape != q.shape or out_gate.dtype != q.dtype):
+            raise ValueError("out_gate must match o")
+        rc = lib.sparse_attn_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
+                                       _ptr(alpha), _ptr(out), B, Hq, Hkv, Lmax, d, dt, m,
+                                       int(k_win), int(pi), int(M), int(seg), ctypes.byref(opt), _ptr(ws),
+                                       nbytes if ws is not None else 0, _stream(q.device))
+        if rc != SA_OK:
+            _raise(lib, rc, "sparse_attn_decode_ex")
+        return out
     rc = lib.sparse_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
                                 _ptr(alpha), _ptr(out), B, Hq, Hkv, Lmax, d, dt, m,
                                 int(k_win), int(pi), int(M), int(seg), _ptr(ws),

@@ -95,7 +95,8 @@ FwdLayout fwd_layout(int heads, int N, int d, int dtype) {
 }
 
 int fwd_validate(const void *q, const void *k, const void *v, const float *alpha, void *o, int B, int Hq,
-                 int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg) {
+                 int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg,
+                 bool gate_from_q = false) {
   int rc = check_shape(dtype, d);
   if (rc != SA_OK) return rc;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and N must be >= 1");
@@ -103,7 +104,8 @@ int fwd_validate(const void *q, const void *k, const void *v, const float *alpha
   rc = check_mode(mode, k_win, pi, M, seg);
   if (rc != SA_OK) return rc;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return fail(SA_ERR_INVALID, "null tensor pointer");
-  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
+  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr && !gate_from_q)
+    return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 4))
     return fail(SA_ERR_INVALID, "misaligned tensor (q/k/v/o need 16 bytes, alpha 4)");
   const long long rows = (long long)B * Hq * N;
@@ -135,12 +137,59 @@ size_t sparse_attn_fwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int 
 
 namespace {
 
+// Options of the *_ex entry points, as the kernels take them.
+sa::FusedOpts fused_opts(const sa_options *opt, int Hq) {
+  sa::FusedOpts f;
+  f.score_scale = opt != nullptr ? opt->score_scale : 0.f;
+  f.cosine = opt != nullptr && opt->cosine != 0;
+  f.gate_w = opt != nullptr ? opt->gate_w : nullptr;
+  f.gate_b = opt != nullptr ? opt->gate_b : nullptr;
+  f.gate_bh0 = 0;
+  f.gate_hq = Hq;
+  f.out_gate = opt != nullptr ? opt->out_gate : nullptr;
+  return f;
+}
+
+int check_opts(const sa::FusedOpts &f, int mode) {
+  if (!(f.score_scale >= 0.f) || f.score_scale > 3.0e38f) return fail(SA_ERR_INVALID, "score_scale must be finite and >= 0");
+  if ((f.gate_w == nullptr) != (f.gate_b == nullptr)) return fail(SA_ERR_INVALID, "gate_w and gate_b go together");
+  if (f.gate_w != nullptr && mode != SA_MODE_PI) return fail(SA_ERR_INVALID, "the query-driven gate is a PI-mode option");
+  if (!aligned(f.gate_w, 4) || !aligned(f.gate_b, 4) || !aligned(f.out_gate, 16))
+    return fail(SA_ERR_INVALID, "misaligned option tensor");
+  return SA_OK;
+}
+
+// Bytes of the L2-normalised key copy that cosine scores read.
+size_t khat_bytes(const sa::FusedOpts &f, int B, int Hkv, int N, int d, int dtype) {
+  return f.cosine ? round_up((size_t)B * Hkv * N * d * elem_size(dtype), 256) : 0;
+}
+
 int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, void *o, float *lse, int B, int Hq,
              int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg, void *workspace,
-             size_t workspace_bytes, void *stream) {
+             size_t workspace_bytes, void *stream, const sa::FusedOpts &fo = sa::FusedOpts{}) {
   g_err[0] = 0;
-  int rc = fwd_validate(q, k, v, alpha, o, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
+  int rc = fwd_validate(q, k, v, alpha, o, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg,
+                        fo.gate_w != nullptr && mode == SA_MODE_PI);
   if (rc != SA_OK) return rc;
+  rc = check_opts(fo, mode);
+  if (rc != SA_OK) return rc;
+  const size_t kh = khat_bytes(fo, B, Hkv, N, d, dtype);
+  {
+    const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype), nkv = (size_t)B * Hkv * N * d * elem_size(dtype);
+    if (fo.out_gate != nullptr && overlap(o, nq, fo.out_gate, nq)) return fail(SA_ERR_INVALID, "output overlaps out_gate");
+    if (kh > 0) {
+      if (workspace == nullptr || workspace_bytes < kh || !aligned(workspace, 256))
+        return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the forward workspace size");
+      if (overlap(workspace, kh, q, nq) || overlap(workspace, kh, k, nkv) || overlap(workspace, kh, v, nkv) ||
+          overlap(workspace, kh, o, nq))
+        return fail(SA_ERR_INVALID, "workspace overlaps a tensor");
+      hipError_t e = sa::launch_normalize_rows(k, workspace, (long long)B * Hkv * N, d, dtype, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+      k = workspace;   // scores read the normalised keys
+      workspace = (char *)workspace + kh;
+      workspace_bytes -= kh;
+    }
+  }
   if (lse != nullptr) {
     if (!aligned(lse, 4)) return fail(SA_ERR_INVALID, "misaligned lse");
     const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype), nl = (size_t)B * Hq * N * sizeof(float);
@@ -156,6 +205,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
   pa.B = B; pa.Hq = Hq; pa.Hkv = Hkv; pa.N = N; pa.d = d; pa.dtype = dtype;
   pa.mode = mode; pa.k_win = k_win; pa.seg = seg;
   pa.skip_first = N;
+  pa.opt = fo;
   if (!skips) {
     hipError_t e = sa::launch_prefill(pa, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
@@ -185,6 +235,9 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
     sk.acc = (char *)workspace + L.acc_off;
     sk.B = 1; sk.Hq = n; sk.Hkv = n / grp; sk.N = N; sk.d = d; sk.dtype = dtype;
     sk.pi = pi; sk.M = M; sk.m_min = (int)mm;
+    sk.opt = fo;
+    sk.opt.gate_bh0 = bh0;
+    sk.opt.out_gate = nullptr;
     hipError_t e = sa::launch_skip(sk, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
     sa::PrefillArgs pc = pa;
@@ -195,6 +248,8 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
     pc.skip_acc = sk.acc;
     pc.skip_first = (int)(mm * pi);
     pc.lse = lse != nullptr ? lse + (size_t)bh0 * N : nullptr;
+    pc.opt.gate_bh0 = bh0;
+    if (fo.out_gate != nullptr) pc.opt.out_gate = (const char *)fo.out_gate + (size_t)bh0 * head_elems * es;
     e = sa::launch_prefill(pc, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   }
@@ -221,6 +276,23 @@ int sparse_attn_fwd_lse(const void *q, const void *k, const void *v, const float
   }
   return fwd_impl(q, k, v, alpha, o, lse, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg, workspace,
                   workspace_bytes, stream);
+}
+
+size_t sparse_attn_fwd_ex_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win,
+                                         int pi, int M, int seg, const sa_options *opt) {
+  if (check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || Hq % Hkv != 0 ||
+      check_mode(mode, k_win, pi, M, seg) != SA_OK)
+    return 0;
+  const sa::FusedOpts fo = fused_opts(opt, Hq);
+  return khat_bytes(fo, B, Hkv, N, d, dtype) +
+         sparse_attn_fwd_workspace_size(B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
+}
+
+int sparse_attn_fwd_ex(const void *q, const void *k, const void *v, const float *alpha, void *o, float *lse,
+                       int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M,
+                       int seg, const sa_options *opt, void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, alpha, o, lse, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg, workspace,
+                  workspace_bytes, stream, fused_opts(opt, Hq));
 }
 
 // Backward workspace: D_i and c_i per query row (+16 floats of padding for
@@ -281,11 +353,15 @@ namespace {
 int decode_impl(const void *q, const void *k_cache, const void *v_cache, const int *table, const int *cache_lens,
                 const float *alpha, void *o, int B, int Hq, int Hkv, int Lplan, int d, int dtype, int mode, int k_win,
                 int pi, int M, int seg, int layout, int R, int page_shift, int num_pages, int max_pages,
-                size_t cache_bytes, void *workspace, size_t workspace_bytes, void *stream) {
+                size_t cache_bytes, void *workspace, size_t workspace_bytes, void *stream,
+                const sa::FusedOpts &fo = sa::FusedOpts{}) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || o == nullptr)
     return fail(SA_ERR_INVALID, "null tensor pointer");
   if (layout == sa::kCachePaged && table == nullptr) return fail(SA_ERR_INVALID, "null block table");
-  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr) return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
+  int rc = check_opts(fo, mode);
+  if (rc != SA_OK) return rc;
+  if (mode == SA_MODE_PI && M > 0 && alpha == nullptr && fo.gate_w == nullptr)
+    return fail(SA_ERR_INVALID, "alpha is required for PI mode with M > 0");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
       !aligned(alpha, 4) || !aligned(cache_lens, 4) || !aligned(table, 4))
     return fail(SA_ERR_INVALID, "misaligned tensor");
@@ -313,6 +389,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
   da.nsplit = da.n_wsplit + 1;
   da.layout = layout; da.R = R; da.page_shift = page_shift; da.num_pages = num_pages; da.max_pages = max_pages;
   da.table = table;
+  da.opt = fo;
+  if (fo.out_gate != nullptr && overlap(o, nq, fo.out_gate, nq)) return fail(SA_ERR_INVALID, "output overlaps out_gate");
   hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   return SA_OK;
@@ -356,6 +434,21 @@ int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, 
   const size_t nc = (size_t)B * Hkv * Lmax * d * elem_size(dtype);
   return decode_impl(q, k_cache, v_cache, nullptr, cache_lens, alpha, o, B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi,
                      M, seg, sa::kCacheContig, 0, 0, 0, 0, nc, workspace, workspace_bytes, stream);
+}
+
+int sparse_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,
+                          const float *alpha, void *o, int B, int Hq, int Hkv, int Lmax, int d, int dtype, int mode,
+                          int k_win, int pi, int M, int seg, const sa_options *opt, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  int rc = decode_head_checks(B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  if (dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "decode options take bf16 I/O");
+  if ((long long)B * Hkv * Lmax >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
+  const size_t nc = (size_t)B * Hkv * Lmax * d * 2;
+  return decode_impl(q, k_cache, v_cache, nullptr, cache_lens, alpha, o, B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi,
+                     M, seg, sa::kCacheContig, 0, 0, 0, 0, nc, workspace, workspace_bytes, stream,
+                     fused_opts(opt, Hq));
 }
 
 size_t sparse_attn_decode_ring_workspace_size(int B, int Hq, int Hkv, int R, int d, int dtype, int mode, int k_win,
@@ -410,6 +503,14 @@ int sparse_attn_decode_paged(const void *q, const void *k_pages, const void *v_p
                      workspace_bytes, stream);
 }
 
+size_t sparse_attn_bwd_ex_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win,
+                                         int pi, int M, int seg, const sa_options *opt) {
+  const size_t base = sparse_attn_bwd_workspace_size(B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
+  if (base == 0) return 0;
+  const bool gated = opt != nullptr && opt->out_gate != nullptr;
+  return base + (gated ? round_up((size_t)B * Hq * N * d * 2, 256) : 0);
+}
+
 size_t sparse_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype, int mode, int k_win,
                                       int pi, int M, int seg) {
   if (dtype != SA_DTYPE_BF16 || check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 ||
@@ -422,10 +523,26 @@ int sparse_attn_bwd(const void *q, const void *k, const void *v, const float *al
                     const void *dO, void *dq, void *dk, void *dv, float *dalpha, int B, int Hq, int Hkv, int N, int d,
                     int dtype, int mode, int k_win, int pi, int M, int seg, void *workspace, size_t workspace_bytes,
                     void *stream) {
+  return sparse_attn_bwd_ex(q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, B, Hq, Hkv, N, d, dtype, mode, k_win, pi,
+                            M, seg, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int sparse_attn_bwd_ex(const void *q, const void *k, const void *v, const float *alpha, const void *o,
+                       const float *lse, const void *dO, void *dq, void *dk, void *dv, float *dalpha, int B, int Hq,
+                       int Hkv, int N, int d, int dtype, int mode, int k_win, int pi, int M, int seg,
+                       const sa_options *opt, void *dgate, void *workspace, size_t workspace_bytes, void *stream) {
   g_err[0] = 0;
+  const sa::FusedOpts fo = fused_opts(opt, Hq);
   int rc = check_shape(dtype, d);
   if (rc != SA_OK) return rc;
   if (dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "the backward pass supports bf16 I/O only");
+  rc = check_opts(fo, mode);
+  if (rc != SA_OK) return rc;
+  if (fo.cosine || fo.gate_w != nullptr)
+    return fail(SA_ERR_UNSUPPORTED, "the backward pass takes the score scale and the output gate, not cosine scores or the query-driven gate");
+  const bool out_gated = fo.out_gate != nullptr;
+  if (out_gated && (dgate == nullptr || !aligned(dgate, 16)))
+    return fail(SA_ERR_INVALID, "an output gate needs a 16-byte aligned dgate");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return fail(SA_ERR_INVALID, "B, Hq, Hkv and N must be >= 1");
   if (Hq % Hkv != 0) return fail(SA_ERR_INVALID, "Hq must be a multiple of Hkv");
   rc = check_mode(mode, k_win, pi, M, seg);
@@ -445,18 +562,19 @@ int sparse_attn_bwd(const void *q, const void *k, const void *v, const float *al
   if (rows >= (1LL << 31) || (long long)N * d >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
   const bool skips = has_skips(mode, k_win, pi, M, N);
   const BwdLayout L = bwd_layout(B, Hq, Hkv, N, d, skips);
-  if (workspace == nullptr || workspace_bytes < L.total)
-    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_bwd_workspace_size()");
-  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
   const size_t nq = (size_t)rows * d * 2, nkv = (size_t)B * Hkv * N * d * 2, nr = (size_t)rows * 4;
-  const void *ins[] = {q, k, v, o, dO, lse, alpha, workspace};
-  const size_t insz[] = {nq, nkv, nkv, nq, nq, nr, alpha ? nr : 0, L.total};
-  void *outs[] = {dq, dk, dv, dalpha};
-  const size_t outsz[] = {nq, nkv, nkv, dalpha ? nr : 0};
-  for (int a = 0; a < 4; ++a) {
-    for (int bb = 0; bb < 8; ++bb)
+  const size_t total = L.total + (out_gated ? round_up(nq, 256) : 0);
+  if (workspace == nullptr || workspace_bytes < total)
+    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the backward workspace size");
+  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const void *ins[] = {q, k, v, o, dO, lse, alpha, workspace, fo.out_gate};
+  const size_t insz[] = {nq, nkv, nkv, nq, nq, nr, alpha ? nr : 0, total, out_gated ? nq : 0};
+  void *outs[] = {dq, dk, dv, dalpha, out_gated ? dgate : nullptr};
+  const size_t outsz[] = {nq, nkv, nkv, dalpha ? nr : 0, out_gated ? nq : 0};
+  for (int a = 0; a < 5; ++a) {
+    for (int bb = 0; bb < 9; ++bb)
       if (overlap(outs[a], outsz[a], ins[bb], insz[bb])) return fail(SA_ERR_INVALID, "a gradient overlaps an input or the workspace");
-    for (int bb = 0; bb < 4; ++bb)
+    for (int bb = 0; bb < 5; ++bb)
       if (bb != a && overlap(outs[a], outsz[a], outs[bb], outsz[bb])) return fail(SA_ERR_INVALID, "gradients overlap");
   }
   sa::BwdArgs ba;
@@ -471,6 +589,10 @@ int sparse_attn_bwd(const void *q, const void *k, const void *v, const float *al
   ba.B = B; ba.Hq = Hq; ba.Hkv = Hkv; ba.N = N; ba.d = d;
   ba.mode = mode; ba.k_win = k_win; ba.pi = pi; ba.M = M; ba.seg = seg;
   ba.m_min = skips ? (int)skip_m_min(k_win, pi) : 1;
+  ba.score_scale = fo.score_scale;
+  ba.out_gate = fo.out_gate;
+  ba.dgate = out_gated ? dgate : nullptr;
+  ba.dO_gated = out_gated ? (void *)(w + L.total) : nullptr;
   hipError_t e = sa::launch_bwd(ba, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   return SA_OK;

@@ -60,9 +60,16 @@ struct Params {
   // key (m_min * pi), query- and key-period tiles per residue, wave counts
   int P, skip_first, nqt, nkt, nwork_q, nwork_kv;
   float scale_log2, scale;
+  // output gate y = o * sigmoid(g) (o here is y): the prep pass writes
+  // dO * sigmoid(g) to dO_gated, which the other kernels read as dO, and dg
+  const bf16 *out_gate;
+  bf16 *dgate, *dO_gated;
 };
 
 // ---- D_i = <dO_i, o_i>,  c_i = log2(alpha_i) - lse_i log2(e) -----------------
+// With an output gate y = o * sigmoid(g) the inputs are dY and y: the
+// attention's output gradient is dY * sigmoid(g) (written to dO_gated),
+// D_i = <dY_i * sigmoid(g_i), o_i> = <dY_i, y_i>, and dg = dY * y * (1 - sigmoid(g)).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Params p, long long rows) {
   constexpr int L = 8;                              // lanes per row
@@ -71,13 +78,26 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Params p, long long rows)
   const int part = (int)(tid % L);
   float acc = 0.f;
   if (row < rows) {
-    const bf16 *a = p.dO + row * D + part * (D / L);
-    const bf16 *b = p.o + row * D + part * (D / L);
+    const size_t at = (size_t)row * D + part * (D / L);
+    const bf16 *a = p.dO + at;
+    const bf16 *b = p.o + at;
 #pragma unroll
     for (int c = 0; c < D / L; c += 8) {
       const bf16x8 x = *(const bf16x8 *)(a + c), y = *(const bf16x8 *)(b + c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+      if (p.out_gate != nullptr) {
+        const bf16x8 g = *(const bf16x8 *)(p.out_gate + at + c);
+        bf16x8 dog, dg;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-(float)g[e] * kLog2e));
+          dog[e] = (bf16)((float)x[e] * sg);
+          dg[e] = (bf16)((float)x[e] * (float)y[e] * (1.0f - sg));
+        }
+        *(bf16x8 *)(p.dO_gated + at + c) = dog;
+        *(bf16x8 *)(p.dgate + at + c) = dg;
+      }
     }
   }
   acc += __shfl_xor(acc, 1, 64);
@@ -677,10 +697,14 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
   p.M = a.M; p.m_min = a.m_min; p.seg = a.seg; p.grp = a.Hq / a.Hkv;
   p.nqb = (a.N + BM - 1) / BM;
   p.nkb = (a.N + BM - 1) / BM;
-  p.scale = 1.0f / sqrtf((float)D);
+  p.scale = a.score_scale > 0.f ? a.score_scale : 1.0f / sqrtf((float)D);
   p.scale_log2 = kLog2e * p.scale;
+  p.out_gate = (const bf16 *)a.out_gate;
+  p.dgate = (bf16 *)a.dgate;
+  p.dO_gated = (bf16 *)a.dO_gated;
   const long long rows = (long long)a.B * a.Hq * a.N;
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
+  if (p.out_gate != nullptr) p.dO = p.dO_gated;   // the rest differentiate the ungated attention
   p.P = (a.N + a.pi - 1) / (a.pi > 0 ? a.pi : 1);
   p.skip_first = 0;
   p.nqt = p.nkt = p.nwork_q = p.nwork_kv = 0;

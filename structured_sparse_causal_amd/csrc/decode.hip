@@ -39,7 +39,10 @@ struct Params {
   float scale_log2;
   int R, page_shift, num_pages, max_pages;   // ring / paged cache layouts
   const int *table;
+  FusedOpts opt;    // bf16: score scale, cosine, query-driven gate, output gate
 };
+
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e)); }
 
 
 // Rows of this split: count and position of row r.
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   const int fallback = LAYOUT == kCacheContig ? i : 0;   // an in-range physical row
 
   float bias_loc = 0.f, bias_skip = 0.f;   // log2 priors of local and skip keys
-  if (p.mode == kModePi && p.alpha != nullptr && hvalid) {
+  if (p.mode == kModePi && p.alpha != nullptr && p.opt.gate_w == nullptr && hvalid) {
     const float a = p.alpha[(size_t)b * p.Hq + hq];
     bias_loc = __log2f(a);
     bias_skip = __log2f(1.0f - a);
@@ -399,6 +402,31 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   bf16x8 qf[NQF];
 #pragma unroll
   for (int kk = 0; kk < NQF; ++kk) qf[kk] = hvalid ? *(const bf16x8 *)(Qp + 32 * kk + 8 * G) : bf16x8{};
+  float sl2 = p.scale_log2;   // score scale of head column t (log2 units)
+  if (p.opt.cosine || (p.opt.gate_w != nullptr && p.mode == kModePi)) {
+    // lane (G, t) holds dims 32kk + 8G .. +7 of head t; the groups G hold the row
+    const float *w = p.opt.gate_w != nullptr && p.mode == kModePi ? p.opt.gate_w + (size_t)(hvalid ? hq : 0) * D : nullptr;
+    float ss = 0.f, z = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qf[kk][e];
+        ss = fmaf(x, x, ss);
+        if (w != nullptr) z = fmaf(x, w[32 * kk + 8 * G + e], z);
+      }
+    ss += wave_shfl_xor(ss, 16);
+    ss += wave_shfl_xor(ss, 32);
+    z += wave_shfl_xor(z, 16);
+    z += wave_shfl_xor(z, 32);
+    if (p.opt.cosine) sl2 *= hvalid ? rsqrtf(ss) : 0.f;
+    if (w != nullptr && hvalid) {   // alpha = sigmoid(z + b_h): log2 alpha and log2(1 - alpha)
+      z += p.opt.gate_b[hq];
+      const float l1 = __log2f(1.0f + fast_exp2(-fabsf(z) * kLog2e));
+      bias_loc = (z >= 0.f ? 0.f : z * kLog2e) - l1;
+      bias_skip = (z <= 0.f ? 0.f : -z * kLog2e) - l1;
+    }
+  }
 
   f32x4 acc[HC4][NH];
 #pragma unroll
@@ -421,16 +449,29 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // S^T = K Q^T: A fragment = row t, dims 32kk + 8G .. +7.
     f32x4 s = f32x4{};
+    float kss = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NQF; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8 *)(ks + t * LDK + 32 * kk + 8 * G), qf[kk], s, 0,
-                                                   0, 0);
+    for (int kk = 0; kk < NQF; ++kk) {
+      const bf16x8 ka = *(const bf16x8 *)(ks + t * LDK + 32 * kk + 8 * G);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], s, 0, 0, 0);
+      if (p.opt.cosine) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kss = fmaf((float)ka[e], (float)ka[e], kss);
+      }
+    }
+    if (p.opt.cosine) {   // 1/|k| of row t, then of the rows 4G + jj this lane scores
+      kss += wave_shfl_xor(kss, 16);
+      kss += wave_shfl_xor(kss, 32);
+      const float rk = rsqrtf(kss);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) s[jj] *= __shfl(rk, 4 * G + jj, 64);
+    }
     // ---- online softmax per head column (rows r0 + 4G + jj) ----------------
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int rr = r0 + 4 * G + jj;
-      s[jj] = rr < sr.count ? fmaf(s[jj], p.scale_log2, sr.skip_row(rr) ? bias_skip : bias_loc) : -INFINITY;
+      s[jj] = rr < sr.count ? fmaf(s[jj], sl2, sr.skip_row(rr) ? bias_skip : bias_loc) : -INFINITY;
       mx = fmaxf(mx, s[jj]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
@@ -586,7 +627,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(Params p) {
     a = a * f0 + as * f1;
     m = mn;
   }
-  const float o = bad ? NAN : a / l;
+  float o = bad ? NAN : a / l;
+  if constexpr (sizeof(T) == 2) {
+    if (p.opt.out_gate != nullptr) {   // output gate o * sigmoid(g)
+      const unsigned short gu = ((const unsigned short *)p.opt.out_gate)[(size_t)row * D + dim];
+      o *= sigmoid_fast(bf16_to_f32(gu));
+    }
+  }
   T *op = (T *)p.o + (size_t)row * D + dim;
   if constexpr (sizeof(T) == 2) *(unsigned short *)op = f32_to_bf16_bits(o);
   else *op = o;
@@ -601,7 +648,8 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   p.n_wsplit = a.n_wsplit; p.chunk = a.chunk; p.nsplit = a.nsplit;
   p.grp = a.Hq / a.Hkv;
   p.hchunks = (p.grp + 15) / 16;
-  p.scale_log2 = kLog2e / sqrtf((float)D);
+  p.opt = a.opt;
+  p.scale_log2 = kLog2e * (a.opt.score_scale > 0.f ? a.opt.score_scale : 1.0f / sqrtf((float)D));
   p.R = a.R; p.page_shift = a.page_shift; p.num_pages = a.num_pages; p.max_pages = a.max_pages; p.table = a.table;
   const dim3 grid(p.nsplit, a.Hkv * p.hchunks, a.B);
   if constexpr (sizeof(T) == 2) {

@@ -14,6 +14,21 @@ enum { kF32 = 0, kBF16 = 1 };
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
 
+// Fused gate and epilogue options (all off when zero / null):
+//   score_scale > 0 replaces 1/sqrt(d); cosine: scores are scale * cos(q, k)
+//   (the key rows given to the kernels are already L2-normalised; the query's
+//   norm is taken in-kernel); gate_w [Hq][d] / gate_b [Hq]: alpha =
+//   sigmoid(<gate_w[h], q_i> + gate_b[h]) computed in-kernel (PI), where head
+//   h = (gate_bh0 + local (batch, head) index) % gate_hq; out_gate: output
+//   o * sigmoid(out_gate), same layout and dtype as o.
+struct FusedOpts {
+  float score_scale;
+  int cosine;
+  const float *gate_w, *gate_b;
+  int gate_bh0, gate_hq;
+  const void *out_gate;
+};
+
 struct PrefillArgs {
   const void *q, *k, *v;
   const float *alpha;   // [B,Hq,N] or nullptr (PI priors)
@@ -24,6 +39,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, N, d, dtype;
   int mode, k_win, seg;
   int skip_first;       // first query position that has a skip key (PI), else N
+  FusedOpts opt;
 };
 
 struct SkipArgs {
@@ -33,6 +49,7 @@ struct SkipArgs {
   void *acc;            // [B*Hq*N][d] in the I/O dtype
   int B, Hq, Hkv, N, d, dtype;
   int pi, M, m_min;     // skip offsets m*pi for m in [m_min, M]
+  FusedOpts opt;        // score_scale, cosine, gate (out_gate unused)
 };
 
 struct DecodeArgs {
@@ -49,6 +66,7 @@ struct DecodeArgs {
   // block table [B][max_pages] (P = 1 << page_shift, Lmax = max_pages * P).
   int layout, R, page_shift, num_pages, max_pages;
   const int *table;
+  FusedOpts opt;        // bf16 only (gate_bh0 = 0, gate_hq = Hq)
 };
 enum { kCacheContig = 0, kCacheRing = 1, kCachePaged = 2 };
 
@@ -61,7 +79,12 @@ struct BwdArgs {
   float *dq_s, *dk_s, *dv_s; // workspace skip contributions, or nullptr
   int B, Hq, Hkv, N, d;
   int mode, k_win, pi, M, m_min, seg;
+  float score_scale;                // 0: 1/sqrt(d)
+  const void *out_gate;             // output gate g (bf16, like o) or nullptr
+  void *dgate;                      // dL/dg (bf16) when out_gate is given
+  void *dO_gated;                   // workspace [B*Hq*N][d] bf16: dO * sigmoid(g)
 };
+hipError_t launch_normalize_rows(const void *src, void *dst, long long rows, int d, int dtype, hipStream_t s);
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);

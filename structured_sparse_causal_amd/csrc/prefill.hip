@@ -50,7 +50,18 @@ struct Params {
   int rank_group;      // heads walked together in rank order (divides heads_per_xcd)
   int ecp_J, ecp_C;    // ECP blocks per half-segment and half-segments (0: none)
   float scale_log2;
+  FusedOpts opt;
 };
+
+// Gate and epilogue helpers shared by both prefill kernels.
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+}
+
+// log2(sigmoid(z)) without overflow for large |z|.
+__device__ __forceinline__ float log2_sigmoid(float z) {
+  return z >= 0.f ? -__log2f(1.0f + fast_exp2(-z * kLog2e)) : z * kLog2e - __log2f(1.0f + fast_exp2(z * kLog2e));
+}
 
 
 // Work order.  A query block's cost is its number of key tiles, which varies
@@ -135,6 +146,21 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
   float qf[D / 2];
 #pragma unroll
   for (int kk = 0; kk < D / 2; ++kk) qf[kk] = qvalid ? Qp[(size_t)qi * D + 2 * kk + h] : 0.f;
+  float sl2 = p.scale_log2;
+  if (p.opt.cosine) {   // scale * cos(q, k): keys arrive normalised, 1/|q_i| joins this lane's scale
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) ss = fmaf(qf[kk], qf[kk], ss);
+    sl2 *= rsqrtf(half_swap_sum(ss));
+  }
+  if (p.opt.gate_w != nullptr && p.mode == kModePi) {   // alpha = sigmoid(<w_h, q_i> + b_h)
+    const int hg = (p.opt.gate_bh0 + bh) % p.opt.gate_hq;
+    const float *w = p.opt.gate_w + (size_t)hg * D;
+    float z = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) z = fmaf(qf[kk], w[2 * kk + h], z);
+    bias = log2_sigmoid(half_swap_sum(z) + p.opt.gate_b[hg]);
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -164,7 +190,6 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
   const bool wave_live = q0 < N;
   const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
   const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
-  const float sl2 = p.scale_log2;
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t_begin + t * BN;
@@ -240,6 +265,7 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
   if (p.lse != nullptr && h == 0) p.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot)) * kLn2;
   const float inv = 1.0f / l_tot;
   float *op = (float *)p.o + ((size_t)bh * N + qi) * D;
+  const float *gp = p.opt.out_gate != nullptr ? (const float *)p.opt.out_gate + ((size_t)bh * N + qi) * D : nullptr;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -247,6 +273,11 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
       f32x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
+      if (gp != nullptr) {   // output gate o * sigmoid(g)
+        const f32x4 gv = *(const f32x4 *)(gp + 32 * db + 8 * j4 + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] *= sigmoidf_fast(gv[e]);
+      }
       *(f32x4 *)(op + 32 * db + 8 * j4 + 4 * h) = x;
     }
 }
@@ -284,6 +315,25 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
   for (int kk = 0; kk < NQF; ++kk)
     qf[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)qi * D + 16 * kk + 8 * h) : bf16x8{};
+  float sl2 = p.scale_log2;
+  if (p.opt.cosine) {   // scale * cos(q, k): keys arrive normalised, 1/|q_i| joins this lane's scale
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)qf[kk][e], (float)qf[kk][e], ss);
+    sl2 *= rsqrtf(half_swap_sum(ss));
+  }
+  if (p.opt.gate_w != nullptr && p.mode == kModePi) {   // alpha = sigmoid(<w_h, q_i> + b_h)
+    const int hg = (p.opt.gate_bh0 + bh) % p.opt.gate_hq;
+    const float *w = p.opt.gate_w + (size_t)hg * D;
+    float z = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], w[16 * kk + 8 * h + e], z);
+    bias = log2_sigmoid(half_swap_sum(z) + p.opt.gate_b[hg]);
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -319,7 +369,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
   const int w_lo_last = key_lo(min(q0 + 31, N - 1), p.mode, p.k_win, p.seg);
   const bool w_allvalid = q0 + 31 < N;
-  const float sl2 = p.scale_log2;
 
   // ---- direct-to-LDS staging of one K and one V tile -----------------------
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
@@ -460,15 +509,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   if (p.lse != nullptr && h == 0) p.lse[(size_t)bh * N + qi] = (m_run + __log2f(l_tot)) * kLn2;
   const float inv = 1.0f / l_tot;
   bf16 *op = (bf16 *)p.o + ((size_t)bh * N + qi) * D;
+  const bf16 *gp = p.opt.out_gate != nullptr ? (const bf16 *)p.opt.out_gate + ((size_t)bh * N + qi) * D : nullptr;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
+      if (gp != nullptr) {   // output gate o * sigmoid(g)
+        const ushort4 gu = *(const ushort4 *)(gp + 32 * db + 8 * j4 + 4 * h);
+        x[0] *= sigmoidf_fast(bf16_to_f32(gu.x));
+        x[1] *= sigmoidf_fast(bf16_to_f32(gu.y));
+        x[2] *= sigmoidf_fast(bf16_to_f32(gu.z));
+        x[3] *= sigmoidf_fast(bf16_to_f32(gu.w));
+      }
       ushort4 u;
-      u.x = f32_to_bf16_bits(acc[db][4 * j4 + 0] * inv);
-      u.y = f32_to_bf16_bits(acc[db][4 * j4 + 1] * inv);
-      u.z = f32_to_bf16_bits(acc[db][4 * j4 + 2] * inv);
-      u.w = f32_to_bf16_bits(acc[db][4 * j4 + 3] * inv);
+      u.x = f32_to_bf16_bits(x[0]);
+      u.y = f32_to_bf16_bits(x[1]);
+      u.z = f32_to_bf16_bits(x[2]);
+      u.w = f32_to_bf16_bits(x[3]);
       *(ushort4 *)(op + 32 * db + 8 * j4 + 4 * h) = u;
     }
 }
@@ -505,13 +565,56 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
     p.ecp_J = a.seg / BM;
     p.ecp_C = a.N / a.seg;
   }
-  p.scale_log2 = kLog2e / sqrtf((float)D);
+  p.opt = a.opt;
+  p.scale_log2 = kLog2e * (a.opt.score_scale > 0.f ? a.opt.score_scale : 1.0f / sqrtf((float)D));
   if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
   else hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// L2-normalised copy of key rows (scaled cosine scores): 8 lanes per row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void normalize_rows_kernel(const T *src, T *dst, long long rows) {
+  constexpr int L = 8, C = D / L;
+  const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = tid / L;
+  const int part = (int)(tid % L);
+  const long long r = row < rows ? row : rows - 1;
+  float x[C], ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    x[c] = to_f32<T>(src[r * D + part * C + c]);
+    ss = fmaf(x[c], x[c], ss);
+  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  const float inv = rsqrtf(ss);
+  if (row >= rows) return;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    if constexpr (sizeof(T) == 2) {
+      const unsigned short u = f32_to_bf16_bits(x[c] * inv);
+      dst[r * D + part * C + c] = __builtin_bit_cast(bf16, u);
+    } else {
+      dst[r * D + part * C + c] = x[c] * inv;
+    }
+  }
+}
+
+hipError_t launch_normalize_rows(const void *src, void *dst, long long rows, int d, int dtype, hipStream_t s) {
+  const dim3 grid((unsigned)((rows * 8 + 255) / 256));
+  if (dtype == kBF16) {
+    if (d == 64) hipLaunchKernelGGL((normalize_rows_kernel<bf16, 64>), grid, dim3(256), 0, s, (const bf16 *)src, (bf16 *)dst, rows);
+    else hipLaunchKernelGGL((normalize_rows_kernel<bf16, 128>), grid, dim3(256), 0, s, (const bf16 *)src, (bf16 *)dst, rows);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((normalize_rows_kernel<float, 64>), grid, dim3(256), 0, s, (const float *)src, (float *)dst, rows);
+    else hipLaunchKernelGGL((normalize_rows_kernel<float, 128>), grid, dim3(256), 0, s, (const float *)src, (float *)dst, rows);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   if (a.dtype == kBF16) return a.d == 64 ? launch_t<bf16, 64>(a, s) : launch_t<bf16, 128>(a, s);

@@ -32,7 +32,13 @@ struct Params {
   int ntiles;     // query-period tiles of 16 per residue
   int nwork;      // B*Hq*pi*ntiles work items (one per wave)
   float scale_log2;
+  FusedOpts opt;  // cosine (keys arrive normalised) and the query-driven gate
 };
+
+// log2(1 - sigmoid(z)) = log2(sigmoid(-z)) without overflow for large |z|.
+__device__ __forceinline__ float log2_one_minus_sigmoid(float z) {
+  return z <= 0.f ? -__log2f(1.0f + fast_exp2(z * kLog2e)) : -z * kLog2e - __log2f(1.0f + fast_exp2(-z * kLog2e));
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
@@ -61,7 +67,29 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
   for (int kk = 0; kk < D / 32; ++kk)
     qf[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
   float bias = -INFINITY;  // log2(1 - alpha)
-  if (qvalid) bias = __log2f(1.0f - p.alpha[(size_t)bh * N + iq]);
+  if (qvalid && p.opt.gate_w == nullptr) bias = __log2f(1.0f - p.alpha[(size_t)bh * N + iq]);
+  float sl2 = p.scale_log2;
+  if (p.opt.cosine || p.opt.gate_w != nullptr) {
+    // this lane holds dims 32kk + 8G .. +7 of query column t; the four lane
+    // groups G together hold the row
+    const int hg = p.opt.gate_w != nullptr ? (p.opt.gate_bh0 + bh) % p.opt.gate_hq : 0;
+    const float *w = p.opt.gate_w != nullptr ? p.opt.gate_w + (size_t)hg * D : nullptr;
+    float ss = 0.f, z = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qf[kk][e];
+        ss = fmaf(x, x, ss);
+        if (w != nullptr) z = fmaf(x, w[32 * kk + 8 * G + e], z);
+      }
+    ss += wave_shfl_xor(ss, 16);
+    ss += wave_shfl_xor(ss, 32);
+    z += wave_shfl_xor(z, 16);
+    z += wave_shfl_xor(z, 32);
+    if (p.opt.cosine) sl2 *= rsqrtf(ss);
+    if (w != nullptr && qvalid) bias = log2_one_minus_sigmoid(z + p.opt.gate_b[hg]);
+  }
 
   f32x4 acc[D / 16];
 #pragma unroll
@@ -98,7 +126,7 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
     for (int jj = 0; jj < 4; ++jj) {
       const int m = pq - (kt + 4 * G + jj);
       const bool ok = qvalid && m >= p.m_min && m <= p.M;
-      s[jj] = ok ? s[jj] * p.scale_log2 + bias : -INFINITY;
+      s[jj] = ok ? s[jj] * sl2 + bias : -INFINITY;
       mx = fmaxf(mx, s[jj]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
@@ -165,7 +193,20 @@ __global__ __launch_bounds__(128) void skip_f32_kernel(Params p, int first, long
   const float *Qp = (const float *)p.q + ((size_t)bh * p.N + i) * D;
   const float *Kp = (const float *)p.k + (size_t)(b * p.Hkv + g) * p.N * D;
   const float *Vp = (const float *)p.v + (size_t)(b * p.Hkv + g) * p.N * D;
-  const float bias = __log2f(1.0f - p.alpha[(size_t)bh * p.N + i]);
+  float bias, sl2 = p.scale_log2;
+  if (p.opt.gate_w != nullptr) {   // alpha = sigmoid(<w_h, q_i> + b_h)
+    const int hg = (p.opt.gate_bh0 + bh) % p.opt.gate_hq;
+    float z = p.opt.gate_b[hg];
+    for (int c = 0; c < D; ++c) z = fmaf(Qp[c], p.opt.gate_w[(size_t)hg * D + c], z);
+    bias = log2_one_minus_sigmoid(z);
+  } else {
+    bias = __log2f(1.0f - p.alpha[(size_t)bh * p.N + i]);
+  }
+  if (p.opt.cosine) {   // keys arrive normalised; 1/|q_i| joins the scale
+    float ss = 0.f;
+    for (int c = 0; c < D; ++c) ss = fmaf(Qp[c], Qp[c], ss);
+    sl2 *= rsqrtf(ss);
+  }
   float acc[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) acc[c] = 0.f;
@@ -175,7 +216,7 @@ __global__ __launch_bounds__(128) void skip_f32_kernel(Params p, int first, long
     if (j < 0) break;
     float dot = 0.f;
     for (int c = 0; c < D; ++c) dot = fmaf(Qp[c], Kp[(size_t)j * D + c], dot);
-    const float sc = dot * p.scale_log2 + bias;
+    const float sc = dot * sl2 + bias;
     const float mr = fmaxf(m_run, sc);
     const float f = fast_exp2(m_run - mr);
     const float pv = fast_exp2(sc - mr);
@@ -197,7 +238,8 @@ hipError_t launch_t(const SkipArgs &a, hipStream_t s) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.ml = a.ml; p.acc = a.acc;
   p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.pi = a.pi; p.M = a.M; p.m_min = a.m_min;
   p.P = (a.N + a.pi - 1) / a.pi;
-  p.scale_log2 = kLog2e / sqrtf((float)D);
+  p.opt = a.opt;
+  p.scale_log2 = kLog2e * (a.opt.score_scale > 0.f ? a.opt.score_scale : 1.0f / sqrtf((float)D));
   const int first = a.m_min * a.pi;  // first position with a skip key
   if (first >= a.N) return hipSuccess;
   if (a.dtype == kBF16) {

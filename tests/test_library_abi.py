@@ -285,3 +285,60 @@ def test_further_mask_modes_validation(lib):
     # s-Split decodes: split plan over the seg rows of the query's segment
     assert lib.sparse_attn_decode_workspace_size(2, 8, 2, 512, 128, BF16, SSPLIT, 0, 0, 0, 300) == \
         256 * ((2 * 8 * 3 * 132 * 4 + 255) // 256)
+
+
+def opts(score_scale=0.0, cosine=0, gate_w=None, gate_b=None, out_gate=None):
+    return ctypes.byref(binding.SaOptions(score_scale, cosine, gate_w, gate_b, out_gate))
+
+
+def fwd_ex(lib, opt, q=Q, k=K, v=V, a=A, o=O, lse=None, B=1, Hq=2, Hkv=2, N=256, d=64, dtype=BF16, mode=WINDOW,
+           k_win=32, pi=64, M=3, seg=0, ws=WS, wsb=1 << 30):
+    return lib.sparse_attn_fwd_ex(q, k, v, a, o, lse, B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg, opt,
+                                  ws, wsb, None)
+
+
+GW, GB, OG = 0x40000000, 0x40001000, 0x50000000
+
+
+@pytest.mark.parametrize("kw,okw,code", [
+    (dict(), dict(score_scale=-1.0), INVALID), (dict(), dict(score_scale=float("nan")), INVALID),
+    (dict(mode=PI), dict(gate_w=GW), INVALID),                 # gate_w without gate_b
+    (dict(), dict(gate_w=GW, gate_b=GB), INVALID),             # the gate is a PI-mode option
+    (dict(mode=PI), dict(gate_w=GW + 2, gate_b=GB), INVALID),  # misaligned
+    (dict(), dict(out_gate=OG + 8), INVALID), (dict(), dict(out_gate=O + 64), INVALID),
+    (dict(ws=None, wsb=0), dict(cosine=1), WORKSPACE), (dict(ws=WS, wsb=1000), dict(cosine=1), WORKSPACE),
+    (dict(ws=K + 256), dict(cosine=1), INVALID),                # the key copy would overlap k
+])
+def test_fwd_ex_rejects(lib, kw, okw, code):
+    assert fwd_ex(lib, opts(**okw), **kw) == code
+
+
+def test_fwd_ex_accepts_gate_without_alpha(lib):
+    # PI with the query-driven gate needs no alpha: validation runs to the overlap check
+    assert fwd_ex(lib, opts(gate_w=GW, gate_b=GB), mode=PI, a=None, o=Q) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+
+
+def test_ex_workspace_sizes(lib):
+    r256 = lambda x: -(-x // 256) * 256
+    f = lib.sparse_attn_fwd_ex_workspace_size
+    assert f(1, 2, 2, 256, 64, BF16, WINDOW, 32, 0, 0, 0, None) == 0
+    assert f(1, 2, 2, 256, 64, BF16, WINDOW, 32, 0, 0, 0, opts(score_scale=0.3)) == 0
+    assert f(1, 4, 2, 256, 64, BF16, WINDOW, 32, 0, 0, 0, opts(cosine=1)) == r256(2 * 256 * 64 * 2)
+    assert f(2, 16, 16, 16384, 64, BF16, PI, 256, 1024, 15, 0, opts(cosine=1)) == \
+        r256(32 * 16384 * 64 * 2) + lib.sparse_attn_fwd_workspace_size(2, 16, 16, 16384, 64, BF16, PI, 256, 1024, 15, 0)
+    b = lib.sparse_attn_bwd_ex_workspace_size
+    base = lib.sparse_attn_bwd_workspace_size(1, 2, 2, 256, 64, BF16, WINDOW, 32, 0, 0, 0)
+    assert b(1, 2, 2, 256, 64, BF16, WINDOW, 32, 0, 0, 0, None) == base
+    assert b(1, 2, 2, 256, 64, BF16, WINDOW, 32, 0, 0, 0, opts(out_gate=OG)) == base + r256(2 * 256 * 64 * 2)
+
+
+def test_bwd_ex_and_decode_ex_rejects(lib):
+    args = (Q, K, V, A, O, LSE, DO, DQ, DK, DV, DA, 1, 2, 2, 256, 64, BF16, PI, 32, 64, 3, 0)
+    assert lib.sparse_attn_bwd_ex(*args, opts(cosine=1), None, WS, 1 << 30, None) == UNSUPPORTED
+    assert lib.sparse_attn_bwd_ex(*args, opts(gate_w=GW, gate_b=GB), None, WS, 1 << 30, None) == UNSUPPORTED
+    assert lib.sparse_attn_bwd_ex(*args, opts(out_gate=OG), None, WS, 1 << 30, None) == INVALID   # no dgate
+    assert lib.sparse_attn_bwd_ex(*args, opts(out_gate=OG), DQ + 64, WS, 1 << 30, None) == INVALID  # dgate overlaps dq
+    dargs = (Q, K, V, A, A + 4096, O, 2, 8, 2, 512, 128)
+    assert lib.sparse_attn_decode_ex(*dargs, F32, PI, 64, 64, 3, 0, opts(score_scale=0.1), WS, 1 << 30, None) == UNSUPPORTED
+    assert lib.sparse_attn_decode_ex(*dargs, BF16, PI, 64, 64, 3, 0, opts(out_gate=O + 16), WS, 1 << 30, None) == INVALID
