@@ -285,6 +285,62 @@ def run_decode_layouts(torch, sa, w, reps, warmup):
     return res
 
 
+def run_option_workloads(torch, sa, reps, warmup):
+    """Fused gate and epilogue options at the benchmark shapes, each timed
+    against the plain call on the same inputs (same useful FLOP or bytes):
+    cosine scores (ECP), the query-driven gate (pi-Attention), the output
+    gate (ECP), and all three in the GQA decode."""
+    from structured_sparse_causal_amd.inputs import WORKLOADS, decode_inputs, prefill_inputs
+    dev = torch.device("cuda:0")
+    res = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        return float(np.median(event_times(torch, fn, reps)))
+
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(99)
+    for name, wname, opt in (("ecp_cosine", "ecp_bf16", "cosine"), ("pi_query_gate", "pi_bf16", "gate"),
+                             ("ecp_out_gate", "ecp_bf16", "out_gate")):
+        w = WORKLOADS[wname]
+        q, k, v, a = prefill_inputs(w, device=dev)
+        prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+        out = torch.empty_like(q)
+        kw = {}
+        if opt == "cosine":
+            kw = dict(cosine=True, score_scale=10.0)
+        elif opt == "gate":
+            kw = dict(gate_w=(0.5 * torch.randn((w.Hq, w.d), generator=gen) / math.sqrt(w.d)).to(dev),
+                      gate_b=torch.randn((w.Hq,), generator=gen).to(dev))
+        else:
+            kw = dict(out_gate=torch.randn(q.shape, generator=gen).to(q.dtype).to(dev))
+        alpha = None if opt == "gate" else a
+        ms_plain = timed(lambda: sa.fwd(q, k, v, a, out=out, **prm))
+        ms_opt = timed(lambda: sa.fwd(q, k, v, alpha, out=out, **prm, **kw))
+        flop, _ = prefill_useful(w)
+        res[name] = {"ms": ms_opt, "ms_plain": ms_plain, "useful_tflops": flop / (ms_opt * 1e-3) / 1e12,
+                     "overhead_pct": 100.0 * (ms_opt / ms_plain - 1.0)}
+        del q, k, v, a, out, kw
+        torch.cuda.empty_cache()
+    w = WORKLOADS["decode_pi_gqa_bf16"]
+    q, kc, vc, lens, a = decode_inputs(w, device=dev)
+    prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+    out = torch.empty_like(q)
+    kw = dict(cosine=True, score_scale=10.0,
+              gate_w=(0.5 * torch.randn((w.Hq, w.d), generator=gen) / math.sqrt(w.d)).to(dev),
+              gate_b=torch.randn((w.Hq,), generator=gen).to(dev),
+              out_gate=torch.randn(q.shape, generator=gen).to(q.dtype).to(dev))
+    ms_plain = timed(lambda: sa.decode(q, kc, vc, lens, a, out=out, **prm))
+    ms_opt = timed(lambda: sa.decode(q, kc, vc, lens, None, out=out, **prm, **kw))
+    _, nb = decode_useful(w)
+    res["decode_all_options"] = {"ms": ms_opt, "ms_plain": ms_plain, "useful_GBps": nb / (ms_opt * 1e-3) / 1e9,
+                                 "overhead_pct": 100.0 * (ms_opt / ms_plain - 1.0)}
+    del q, kc, vc, lens, a, out, kw
+    return res
+
+
 def run_bwd_workload(torch, sa, w, reps, warmup):
     """Backward pass of one layer call (bf16): gradients of q, k, v (and
     alpha) given dO, from the o and lse of a training forward run before the
@@ -379,6 +435,10 @@ def main():
     sa.load_library()
     dev = torch.device("cuda:0")
     if args.only is not None:
+        if args.only == "fused_options":
+            print(json.dumps({"workload": args.only, **run_option_workloads(torch, sa, args.steps, args.warmup)}),
+                  flush=True)
+            return
         if args.only == "decode_layouts":
             print(json.dumps({"workload": args.only,
                               **run_decode_layouts(torch, sa, WORKLOADS["decode_pi_gqa_bf16"], args.steps,
@@ -476,6 +536,11 @@ def main():
             extras[name] = run_prefill_workload(torch, sa, wx, 10 if wx.d == 128 else 30, 3)
             log("  %s" % json.dumps(extras[name]))
             torch.cuda.empty_cache()
+        # Fused gate and epilogue options against the plain calls.
+        log("bench: fused options")
+        extras["fused_options"] = run_option_workloads(torch, sa, 20, 3)
+        log("  %s" % json.dumps(extras["fused_options"]))
+        torch.cuda.empty_cache()
         # Serving decode: cache layouts, and throughput over cache lengths.
         wd = WORKLOADS["decode_pi_gqa_bf16"]
         log("bench: decode over paged and ring caches")

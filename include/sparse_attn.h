@@ -242,7 +242,7 @@ int sparse_attn_decode_paged(const void *q, const void *k_pages, const void *v_p
  *                section 2 item 3: a light per-token, per-head network; read
  *                here as one linear layer per head on the query), and the
  *                alpha argument is ignored.  gate_w fp32 [Hq, d], gate_b fp32
- *                [Hq], device memory, 4-byte aligned; both or neither.
+ *                [Hq], device memory (gate_w 16-byte, gate_b 4-byte aligned); both or neither.
  *   out_gate     output gate of the LT2 page (section 3): the result is
  *                o * sigmoid(out_gate), out_gate shaped and typed like o
  *                (decode: [B, Hq, d]), device memory, 16-byte aligned.

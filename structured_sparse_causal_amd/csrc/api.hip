@@ -154,7 +154,7 @@ int check_opts(const sa::FusedOpts &f, int mode) {
   if (!(f.score_scale >= 0.f) || f.score_scale > 3.0e38f) return fail(SA_ERR_INVALID, "score_scale must be finite and >= 0");
   if ((f.gate_w == nullptr) != (f.gate_b == nullptr)) return fail(SA_ERR_INVALID, "gate_w and gate_b go together");
   if (f.gate_w != nullptr && mode != SA_MODE_PI) return fail(SA_ERR_INVALID, "the query-driven gate is a PI-mode option");
-  if (!aligned(f.gate_w, 4) || !aligned(f.gate_b, 4) || !aligned(f.out_gate, 16))
+  if (!aligned(f.gate_w, 16) || !aligned(f.gate_b, 4) || !aligned(f.out_gate, 16))
     return fail(SA_ERR_INVALID, "misaligned option tensor");
   return SA_OK;
 }

@@ -402,32 +402,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   bf16x8 qf[NQF];
 #pragma unroll
   for (int kk = 0; kk < NQF; ++kk) qf[kk] = hvalid ? *(const bf16x8 *)(Qp + 32 * kk + 8 * G) : bf16x8{};
-  float sl2 = p.scale_log2;   // score scale of head column t (log2 units)
-  if (p.opt.cosine || (p.opt.gate_w != nullptr && p.mode == kModePi)) {
-    // lane (G, t) holds dims 32kk + 8G .. +7 of head t; the groups G hold the row
-    const float *w = p.opt.gate_w != nullptr && p.mode == kModePi ? p.opt.gate_w + (size_t)(hvalid ? hq : 0) * D : nullptr;
-    float ss = 0.f, z = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NQF; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)qf[kk][e];
-        ss = fmaf(x, x, ss);
-        if (w != nullptr) z = fmaf(x, w[32 * kk + 8 * G + e], z);
-      }
-    ss += wave_shfl_xor(ss, 16);
-    ss += wave_shfl_xor(ss, 32);
-    z += wave_shfl_xor(z, 16);
-    z += wave_shfl_xor(z, 32);
-    if (p.opt.cosine) sl2 *= hvalid ? rsqrtf(ss) : 0.f;
-    if (w != nullptr && hvalid) {   // alpha = sigmoid(z + b_h): log2 alpha and log2(1 - alpha)
-      z += p.opt.gate_b[hq];
-      const float l1 = __log2f(1.0f + fast_exp2(-fabsf(z) * kLog2e));
-      bias_loc = (z >= 0.f ? 0.f : z * kLog2e) - l1;
-      bias_skip = (z <= 0.f ? 0.f : -z * kLog2e) - l1;
-    }
-  }
-
+  float sl2 = p.scale_log2;   // score scale of head column t (log2 units), set below
   f32x4 acc[HC4][NH];
 #pragma unroll
   for (int c4 = 0; c4 < HC4; ++c4)
@@ -454,9 +429,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
     for (int kk = 0; kk < NQF; ++kk) {
       const bf16x8 ka = *(const bf16x8 *)(ks + t * LDK + 32 * kk + 8 * G);
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], s, 0, 0, 0);
-      if (p.opt.cosine) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kss = fmaf((float)ka[e], (float)ka[e], kss);
+      if (p.opt.cosine) {   // |k|^2 with packed bf16 dot products
+        const bf16x2 x0 = __builtin_shufflevector(ka, ka, 0, 1), x1 = __builtin_shufflevector(ka, ka, 2, 3);
+        const bf16x2 x2 = __builtin_shufflevector(ka, ka, 4, 5), x3 = __builtin_shufflevector(ka, ka, 6, 7);
+        kss = __builtin_amdgcn_fdot2_f32_bf16(x0, x0, kss, false);
+        kss = __builtin_amdgcn_fdot2_f32_bf16(x1, x1, kss, false);
+        kss = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, kss, false);
+        kss = __builtin_amdgcn_fdot2_f32_bf16(x3, x3, kss, false);
       }
     }
     if (p.opt.cosine) {   // 1/|k| of row t, then of the rows 4G + jj this lane scores
@@ -532,6 +511,43 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   Group<D> ring[kRing];
 #pragma unroll
   for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, rm, 16 * wave + j * kStep, lane, fallback);
+  // Cosine scale and query-driven gate, computed while the first rows load
+  // (their global reads would otherwise delay the row stream).
+  if (p.opt.cosine) {
+    // lane (G, t) holds dims 32kk + 8G .. +7 of head t; the groups G hold the row
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)qf[kk][e], (float)qf[kk][e], ss);
+    ss += wave_shfl_xor(ss, 16);
+    ss += wave_shfl_xor(ss, 32);
+    sl2 *= hvalid ? rsqrtf(ss) : 0.f;
+  }
+  if (p.opt.gate_w != nullptr && p.mode == kModePi) {   // alpha = sigmoid(<w_h, q> + b_h)
+    const float *w = p.opt.gate_w + (size_t)(hvalid ? hq : 0) * D + 8 * G;
+    f32x4 wv[NQF][2];
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk) {
+      wv[kk][0] = *(const f32x4 *)(w + 32 * kk);
+      wv[kk][1] = *(const f32x4 *)(w + 32 * kk + 4);
+    }
+    const float bh = p.opt.gate_b[hvalid ? hq : 0];
+    float z = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], wv[kk][e >> 2][e & 3], z);
+    z += wave_shfl_xor(z, 16);
+    z += wave_shfl_xor(z, 32);
+    if (hvalid) {   // log2 alpha and log2(1 - alpha), overflow-free
+      z += bh;
+      const float l1 = __log2f(1.0f + fast_exp2(-fabsf(z) * kLog2e));
+      bias_loc = (z >= 0.f ? 0.f : z * kLog2e) - l1;
+      bias_skip = (z <= 0.f ? 0.f : -z * kLog2e) - l1;
+    }
+  }
+
   for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {

@@ -326,12 +326,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   }
   if (p.opt.gate_w != nullptr && p.mode == kModePi) {   // alpha = sigmoid(<w_h, q_i> + b_h)
     const int hg = (p.opt.gate_bh0 + bh) % p.opt.gate_hq;
-    const float *w = p.opt.gate_w + (size_t)hg * D;
+    const float *w = p.opt.gate_w + (size_t)hg * D + 8 * h;
+    f32x4 wv[NQF][2];
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk) {
+      wv[kk][0] = *(const f32x4 *)(w + 16 * kk);
+      wv[kk][1] = *(const f32x4 *)(w + 16 * kk + 4);
+    }
     float z = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NQF; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], w[16 * kk + 8 * h + e], z);
+      for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], wv[kk][e >> 2][e & 3], z);
     bias = log2_sigmoid(half_swap_sum(z) + p.opt.gate_b[hg]);
   }
 
@@ -574,33 +580,41 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// L2-normalised copy of key rows (scaled cosine scores): 8 lanes per row.
+// L2-normalised copy of key rows (scaled cosine scores): 8 lanes per row,
+// 16-byte loads and stores.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void normalize_rows_kernel(const T *src, T *dst, long long rows) {
-  constexpr int L = 8, C = D / L;
+  constexpr int L = 8, C = D / L;           // elements per lane
+  constexpr int V = 16 / sizeof(T);         // elements per 16-byte chunk
+  typedef T vec __attribute__((ext_vector_type(V)));
   const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = tid / L;
   const int part = (int)(tid % L);
   const long long r = row < rows ? row : rows - 1;
-  float x[C], ss = 0.f;
+  const T *sp = src + r * D + part * C;
+  vec x[C / V];
+  float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    x[c] = to_f32<T>(src[r * D + part * C + c]);
-    ss = fmaf(x[c], x[c], ss);
+  for (int u = 0; u < C / V; ++u) {
+    x[u] = *(const vec *)(sp + u * V);
+#pragma unroll
+    for (int e = 0; e < V; ++e) ss = fmaf(to_f32<T>(x[u][e]), to_f32<T>(x[u][e]), ss);
   }
   ss += __shfl_xor(ss, 1, 64);
   ss += __shfl_xor(ss, 2, 64);
   ss += __shfl_xor(ss, 4, 64);
   const float inv = rsqrtf(ss);
   if (row >= rows) return;
+  T *dp = dst + r * D + part * C;
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    if constexpr (sizeof(T) == 2) {
-      const unsigned short u = f32_to_bf16_bits(x[c] * inv);
-      dst[r * D + part * C + c] = __builtin_bit_cast(bf16, u);
-    } else {
-      dst[r * D + part * C + c] = x[c] * inv;
+  for (int u = 0; u < C / V; ++u) {
+    vec y;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      if constexpr (sizeof(T) == 2) y[e] = __builtin_bit_cast(bf16, f32_to_bf16_bits(to_f32<T>(x[u][e]) * inv));
+      else y[e] = x[u][e] * inv;
     }
+    *(vec *)(dp + u * V) = y;
   }
 }
 

@@ -69,26 +69,35 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
   float bias = -INFINITY;  // log2(1 - alpha)
   if (qvalid && p.opt.gate_w == nullptr) bias = __log2f(1.0f - p.alpha[(size_t)bh * N + iq]);
   float sl2 = p.scale_log2;
-  if (p.opt.cosine || p.opt.gate_w != nullptr) {
-    // this lane holds dims 32kk + 8G .. +7 of query column t; the four lane
-    // groups G together hold the row
-    const int hg = p.opt.gate_w != nullptr ? (p.opt.gate_bh0 + bh) % p.opt.gate_hq : 0;
-    const float *w = p.opt.gate_w != nullptr ? p.opt.gate_w + (size_t)hg * D : nullptr;
-    float ss = 0.f, z = 0.f;
+  // this lane holds dims 32kk + 8G .. +7 of query column t; the four lane
+  // groups G together hold the row
+  if (p.opt.cosine) {
+    float ss = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)qf[kk][e];
-        ss = fmaf(x, x, ss);
-        if (w != nullptr) z = fmaf(x, w[32 * kk + 8 * G + e], z);
-      }
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)qf[kk][e], (float)qf[kk][e], ss);
     ss += wave_shfl_xor(ss, 16);
     ss += wave_shfl_xor(ss, 32);
+    sl2 *= rsqrtf(ss);
+  }
+  if (p.opt.gate_w != nullptr) {   // alpha = sigmoid(<w_h, q_i> + b_h)
+    const int hg = (p.opt.gate_bh0 + bh) % p.opt.gate_hq;
+    const float *w = p.opt.gate_w + (size_t)hg * D + 8 * G;
+    f32x4 wv[D / 32][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      wv[kk][0] = *(const f32x4 *)(w + 32 * kk);
+      wv[kk][1] = *(const f32x4 *)(w + 32 * kk + 4);
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], wv[kk][e >> 2][e & 3], z);
     z += wave_shfl_xor(z, 16);
     z += wave_shfl_xor(z, 32);
-    if (p.opt.cosine) sl2 *= rsqrtf(ss);
-    if (w != nullptr && qvalid) bias = log2_one_minus_sigmoid(z + p.opt.gate_b[hg]);
+    if (qvalid) bias = log2_one_minus_sigmoid(z + p.opt.gate_b[hg]);
   }
 
   f32x4 acc[D / 16];

@@ -304,7 +304,7 @@ GW, GB, OG = 0x40000000, 0x40001000, 0x50000000
     (dict(), dict(score_scale=-1.0), INVALID), (dict(), dict(score_scale=float("nan")), INVALID),
     (dict(mode=PI), dict(gate_w=GW), INVALID),                 # gate_w without gate_b
     (dict(), dict(gate_w=GW, gate_b=GB), INVALID),             # the gate is a PI-mode option
-    (dict(mode=PI), dict(gate_w=GW + 2, gate_b=GB), INVALID),  # misaligned
+    (dict(mode=PI), dict(gate_w=GW + 4, gate_b=GB), INVALID),  # misaligned (16 bytes needed)
     (dict(), dict(out_gate=OG + 8), INVALID), (dict(), dict(out_gate=O + 64), INVALID),
     (dict(ws=None, wsb=0), dict(cosine=1), WORKSPACE), (dict(ws=WS, wsb=1000), dict(cosine=1), WORKSPACE),
     (dict(ws=K + 256), dict(cosine=1), INVALID),                # the key copy would overlap k
