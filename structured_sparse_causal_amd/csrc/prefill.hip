@@ -307,6 +307,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const bf16 *Kp = (const bf16 *)p.k + (size_t)(b * p.Hkv + g) * N * D;
   const bf16 *Vp = (const bf16 *)p.v + (size_t)(b * p.Hkv + g) * N * D;
 
+  // ---- key-tile range ---------------------------------------------------
+  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
+  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
+  const int ntiles = (hi_wg - t_begin) / BN + 1;
+
+  // ---- direct-to-LDS staging of one K and one V tile -----------------------
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  auto stage = [&](int j0, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int slot = PER_WAVE * wave + u;             // 1 KB slot of the tile
+      const int pch = 64 * slot + lane;                 // chunk position in LDS
+      const int row = pch / CPR;
+      const int src = (pch % CPR) ^ tile_swz<D>(row);   // chunk held there
+      const int key = min(j0 + row, N - 1);             // rows past N: masked / probability 0
+      const unsigned voff = (unsigned)((key * D + src * 8) * 2);
+      const unsigned kdst = __builtin_amdgcn_readfirstlane(lds0 + buf * TILE + 1024 * slot);
+      dma16(Kp, voff, kdst);
+      dma16(Vp, voff, kdst + 2 * TILE);
+    }
+  };
+  // The first tile's loads go out before the query's, so the workgroup waits
+  // once for both.
+  stage(t_begin, 0);
+
   const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
   float bias = 0.f;  // log2 of the local prior
   if (p.mode == kModePi && p.alpha != nullptr && qvalid) bias = __log2f(p.alpha[(size_t)bh * N + qi]);
@@ -364,11 +389,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       }
   }
 
-  // ---- key-tile range ---------------------------------------------------
+  // ---- per-wave key range ------------------------------------------------
   const int hi_i = key_hi(qi, N, p.mode, p.k_win, p.seg);
-  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
-  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
-  const int ntiles = (hi_wg - t_begin) / BN + 1;
   const bool wave_live = q0 < N;
   const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
   const int w_hi_first = key_hi(min(q0, N - 1), N, p.mode, p.k_win, p.seg);   // smallest hi of the wave
@@ -376,22 +398,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int w_lo_last = key_lo(min(q0 + 31, N - 1), p.mode, p.k_win, p.seg);
   const bool w_allvalid = q0 + 31 < N;
 
-  // ---- direct-to-LDS staging of one K and one V tile -----------------------
-  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
-  auto stage = [&](int j0, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int slot = PER_WAVE * wave + u;             // 1 KB slot of the tile
-      const int pch = 64 * slot + lane;                 // chunk position in LDS
-      const int row = pch / CPR;
-      const int src = (pch % CPR) ^ tile_swz<D>(row);   // chunk held there
-      const int key = min(j0 + row, N - 1);             // rows past N: masked / probability 0
-      const unsigned voff = (unsigned)((key * D + src * 8) * 2);
-      const unsigned kdst = __builtin_amdgcn_readfirstlane(lds0 + buf * TILE + 1024 * slot);
-      dma16(Kp, voff, kdst);
-      dma16(Vp, voff, kdst + 2 * TILE);
-    }
-  };
 
   // Per-lane LDS byte offsets inside a tile (buffer and key-block offsets are
   // added as constants).  K: row c of a 32-row block, chunk 2kk+h.
@@ -417,12 +423,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     }
   }
 
-  // Settle every compiler-visible load (q, alpha, skip state) here, so no
+  // Settle every load (q, alpha, skip state and the first tile) here, so no
   // wait for them is placed inside the loop, where it would also stall on the
   // in-flight tile.
   __builtin_amdgcn_s_waitcnt(0);
-  stage(t_begin, 0);
-  wait_dma();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {

@@ -40,6 +40,34 @@ __device__ __forceinline__ float log2_one_minus_sigmoid(float z) {
   return z <= 0.f ? -__log2f(1.0f + fast_exp2(z * kLog2e)) : -z * kLog2e - __log2f(1.0f + fast_exp2(-z * kLog2e));
 }
 
+// Loads of one key tile of a residue chain: the K operand row kt + t of this
+// lane and its share of the 16 V rows.  Unconditional: rows past the chain
+// re-read row `safe` (in range); they only ever meet masked scores.  (A
+// predicated load makes the compiler wait for it right after issuing it.)
+template <int D>
+struct KeyTile {
+  bf16x8 k[D / 32];
+  u32x4 v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void load_key_tile(KeyTile<D> &kt_regs, const bf16 *Kp, const bf16 *Vp, int kt, int r,
+                                              int safe, const Params &p, int lane, int G, int t) {
+  const int pk = kt + t;
+  const long long ik = (long long)r + (long long)pk * p.pi;
+  const int ik_ld = (pk < p.P && ik < p.N) ? (int)ik : safe;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) kt_regs.k[kk] = *(const bf16x8 *)(Kp + (size_t)ik_ld * D + 32 * kk + 8 * G);
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+    const int pr = kt + row;
+    const long long ir = (long long)r + (long long)pr * p.pi;
+    const int ir_ld = (pr < p.P && ir < p.N) ? (int)ir : safe;
+    kt_regs.v[u] = *(const u32x4 *)(Vp + (size_t)ir_ld * D + col);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
   constexpr int LD = D + 8;
@@ -62,12 +90,21 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
   const bf16 *Kp = (const bf16 *)p.k + (size_t)(b * p.Hkv + g) * N * D;
   const bf16 *Vp = (const bf16 *)p.v + (size_t)(b * p.Hkv + g) * N * D;
 
+  // Issue the query row, its gate input and the first key tile together; the
+  // prologue below waits for them once.  Row r is in range (r < pi, and some
+  // position has a skip key, so pi < N).
+  // (Key tile first: any wait the compiler places for the query covers it too.)
+  const int kt_lo = max(0, p0 - p.M);
+  const int kt_hi = p0 + 15 - p.m_min;
+  KeyTile<D> tl;
+  load_key_tile<D>(tl, Kp, Vp, kt_lo, r, r, p, lane, G, t);
+  const int iq_ld = qvalid ? iq : r;
   bf16x8 qf[D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    qf[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
+  for (int kk = 0; kk < D / 32; ++kk) qf[kk] = *(const bf16x8 *)(Qp + (size_t)iq_ld * D + 32 * kk + 8 * G);
+  const float a_in = p.opt.gate_w == nullptr ? p.alpha[(size_t)bh * N + iq_ld] : 0.5f;
   float bias = -INFINITY;  // log2(1 - alpha)
-  if (qvalid && p.opt.gate_w == nullptr) bias = __log2f(1.0f - p.alpha[(size_t)bh * N + iq]);
+  if (qvalid && p.opt.gate_w == nullptr) bias = __log2f(1.0f - a_in);
   float sl2 = p.scale_log2;
   // this lane holds dims 32kk + 8G .. +7 of query column t; the four lane
   // groups G together hold the row
@@ -106,27 +143,17 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
   float m_run = kNegBig, l_run = 0.f;
   bf16 *vs = Vs[wave];
 
-  const int kt_lo = max(0, p0 - p.M);
-  const int kt_hi = p0 + 15 - p.m_min;
   for (int kt = kt_lo; kt <= kt_hi; kt += 16) {
+    if (kt != kt_lo) load_key_tile<D>(tl, Kp, Vp, kt, r, r, p, lane, G, t);
     // Key periods kt + 4G + jj (score rows), kt + t (operand rows).
-    const int pk = kt + t;
-    const int ik = r + pk * p.pi;
-    const bool kvalid = pk < p.P && ik < N;
     f32x4 s = f32x4{};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const bf16x8 a = kvalid ? *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], s, 0, 0, 0);
-    }
+    for (int kk = 0; kk < D / 32; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl.k[kk], qf[kk], s, 0, 0, 0);
     // Stage the 16 value rows of this key tile in this wave's LDS slab.
 #pragma unroll
-    for (int ci = lane; ci < 16 * D / 8; ci += 64) {
-      const int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      const int pr = kt + row, ir = r + pr * p.pi;
-      uint4 vv = make_uint4(0, 0, 0, 0);
-      if (pr < p.P && ir < N) vv = *(const uint4 *)(Vp + (size_t)ir * D + col);
-      *(uint4 *)(vs + row * LD + col) = vv;
+    for (int u = 0; u < D / 32; ++u) {
+      const int ci = lane + 64 * u, row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *(u32x4 *)(vs + row * LD + col) = tl.v[u];
     }
     // Band mask: key period pk' = kt + 4G + jj is a skip key of query period pq
     // iff m = pq - pk' lies in [m_min, M].
