@@ -161,16 +161,21 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   const int k0 = 16 * kt;
   const long long ikl = (long long)r + (long long)(k0 + t) * p.pi;
   const bool kvalid = ikl < N;
-  const int ik = kvalid ? (int)ikl : 0;
+  // Rows past the chain re-read row r (in range: r < pi < N) and only meet
+  // masked scores; loads are unconditional so they are issued together.
+  const int ik = kvalid ? (int)ikl : r;
   const bf16 *Kp = p.k + (size_t)bg * N * D, *Vp = p.v + (size_t)bg * N * D;
   bf16 *qs = lds[wave], *os = qs + 16 * LD, *ks = os + 16 * LD;
 
   bf16x8 kf[NK], vf[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    kf[kk] = kvalid ? *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
-    vf[kk] = kvalid ? *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
-    if (WITH_Q) *(bf16x8 *)(ks + t * LD + 32 * kk + 8 * G) = kf[kk];
+    kf[kk] = *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G);
+    vf[kk] = *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G);
+  }
+  if (WITH_Q) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) *(bf16x8 *)(ks + t * LD + 32 * kk + 8 * G) = kf[kk];
   }
   f32x4 adk[ND], adv[ND];
 #pragma unroll
@@ -186,17 +191,17 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
     for (int q0 = q_lo; q0 <= q_hi; q0 += 16) {
       const long long iql = (long long)r + (long long)(q0 + t) * p.pi;
       const bool qvalid = iql < N;
-      const int iq = qvalid ? (int)iql : 0;
+      const int iq = qvalid ? (int)iql : r;   // in-range row; masked below
       const size_t qrow = bh * N + iq;
       bf16x8 qa[NK], oa[NK];
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        qa[kk] = qvalid ? *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
-        oa[kk] = qvalid ? *(const bf16x8 *)(Op + (size_t)iq * D + 32 * kk + 8 * G) : bf16x8{};
+        qa[kk] = *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G);
+        oa[kk] = *(const bf16x8 *)(Op + (size_t)iq * D + 32 * kk + 8 * G);
       }
-      const float c0 = qvalid ? -p.lse[qrow] * kLog2e : 0.f;
-      const float Dq = qvalid ? p.Dv[qrow] : 0.f;
-      const float al = qvalid ? p.alpha[qrow] : 1.f;
+      const float c0 = -p.lse[qrow] * kLog2e;
+      const float Dq = p.Dv[qrow];
+      const float al = p.alpha[qrow];
       f32x4 sc = f32x4{}, dp = f32x4{};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
@@ -290,19 +295,19 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   const int p0 = p.m_min + 16 * tile;
   const long long iql = (long long)r + (long long)(p0 + t) * p.pi;
   const bool qvalid = iql < N;
-  const int iq = qvalid ? (int)iql : 0;
+  const int iq = qvalid ? (int)iql : r;   // in-range row (r < pi < N); masked below
   const size_t qrow = bh * N + iq;
   const bf16 *Kp = p.k + (size_t)(b * p.Hkv + g) * N * D, *Vp = p.v + (size_t)(b * p.Hkv + g) * N * D;
   bf16 *ks = lds[wave];
   bf16x8 qa[NK], oa[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    qa[kk] = qvalid ? *(const bf16x8 *)(p.q + qrow * D + 32 * kk + 8 * G) : bf16x8{};
-    oa[kk] = qvalid ? *(const bf16x8 *)(p.dO + qrow * D + 32 * kk + 8 * G) : bf16x8{};
+    qa[kk] = *(const bf16x8 *)(p.q + qrow * D + 32 * kk + 8 * G);
+    oa[kk] = *(const bf16x8 *)(p.dO + qrow * D + 32 * kk + 8 * G);
   }
-  const float c0 = qvalid ? -p.lse[qrow] * kLog2e : 0.f;
-  const float Dq = qvalid ? p.Dv[qrow] : 0.f;
-  const float al = qvalid ? p.alpha[qrow] : 1.f;
+  const float c0 = -p.lse[qrow] * kLog2e;
+  const float Dq = p.Dv[qrow];
+  const float al = p.alpha[qrow];
   f32x4 aq[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) aq[db] = f32x4{};
@@ -310,13 +315,12 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   const int kt_lo = max(0, p0 - p.M), kt_hi = p0 + 15 - p.m_min;
   for (int kt = kt_lo; kt <= kt_hi; kt += 16) {
     const long long ikl = (long long)r + (long long)(kt + t) * p.pi;
-    const bool kvalid = ikl < N;
-    const int ik = kvalid ? (int)ikl : 0;
+    const int ik = ikl < N ? (int)ikl : r;   // rows past the chain: masked scores
     bf16x8 ka[NK], va[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      ka[kk] = kvalid ? *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
-      va[kk] = kvalid ? *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G) : bf16x8{};
+      ka[kk] = *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G);
+      va[kk] = *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G);
     }
     // element jj: key period kt + 4G + jj, query period p0 + t
     f32x4 st = f32x4{}, dpt = f32x4{};
@@ -436,6 +440,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   const size_t row = (size_t)bh * N + (qvalid ? qi : 0);
   const bf16 *Kp = p.k + (size_t)(b * p.Hkv + g) * N * D;
   const bf16 *Vp = p.v + (size_t)(b * p.Hkv + g) * N * D;
+  const TileOffsets<D> off(lane);
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
+  // The first K/V tile goes out before the query rows: one wait covers both.
+  stage_tile<D>(Kp, t_begin, N - 1, lds0, wave, lane);
+  stage_tile<D>(Vp, t_begin, N - 1, lds0 + 2 * TILE, wave, lane);
 
   bf16x8 qf[NQF], df[NQF];
 #pragma unroll
@@ -451,7 +461,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
 
   const int hi_i = key_hi(qi, N, p.mode, p.k_win, p.seg);
   const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
-  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
   const int ntiles = (hi_wg - t_begin) / BN + 1;
   const bool wave_live = q0 < N;
   const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
@@ -459,13 +468,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   const int w_lo = key_lo(min(q0, N - 1), p.mode, p.k_win, p.seg);
   const int w_lo_last = key_lo(min(q0 + 31, N - 1), p.mode, p.k_win, p.seg);
   const bool w_allvalid = q0 + 31 < N;
-  const TileOffsets<D> off(lane);
-  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
 
-  __builtin_amdgcn_s_waitcnt(0);
-  stage_tile<D>(Kp, t_begin, N - 1, lds0, wave, lane);
-  stage_tile<D>(Vp, t_begin, N - 1, lds0 + 2 * TILE, wave, lane);
-  wait_dma();
+  __builtin_amdgcn_s_waitcnt(0);   // query rows, row scalars and the first tile
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t_begin + t * BN;
