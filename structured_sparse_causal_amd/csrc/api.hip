@@ -297,7 +297,7 @@ int sparse_attn_fwd_ex(const void *q, const void *k, const void *v, const float 
 
 // Backward workspace: D_i and c_i per query row (+16 floats of padding for
 // the 16-byte vector loads at the tail), then, with skip keys, the skip-key
-// contributions in fp32: dq [rows][d], dk and dv [kv rows][d].
+// contributions in bf16: dq [rows][d], dk and dv [kv rows][d].
 struct BwdLayout {
   size_t dv_off, cv_off, dqs_off, dks_off, dvs_off, total;
 };
@@ -310,9 +310,9 @@ static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d, bool skips) {
   L.cv_off = at; at += round_up((rows + 16) * sizeof(float), 256);
   L.dqs_off = L.dks_off = L.dvs_off = 0;
   if (skips) {
-    L.dqs_off = at; at += round_up(rows * d * sizeof(float), 256);
-    L.dks_off = at; at += round_up(kvrows * d * sizeof(float), 256);
-    L.dvs_off = at; at += round_up(kvrows * d * sizeof(float), 256);
+    L.dqs_off = at; at += round_up(rows * d * 2, 256);
+    L.dks_off = at; at += round_up(kvrows * d * 2, 256);
+    L.dvs_off = at; at += round_up(kvrows * d * 2, 256);
   }
   L.total = at;
   return L;
@@ -583,9 +583,9 @@ int sparse_attn_bwd_ex(const void *q, const void *k, const void *v, const float 
   char *w = (char *)workspace;
   ba.Dv = (float *)(w + L.dv_off);
   ba.cv = (float *)(w + L.cv_off);
-  ba.dq_s = skips ? (float *)(w + L.dqs_off) : nullptr;
-  ba.dk_s = skips ? (float *)(w + L.dks_off) : nullptr;
-  ba.dv_s = skips ? (float *)(w + L.dvs_off) : nullptr;
+  ba.dq_s = skips ? (void *)(w + L.dqs_off) : nullptr;
+  ba.dk_s = skips ? (void *)(w + L.dks_off) : nullptr;
+  ba.dv_s = skips ? (void *)(w + L.dvs_off) : nullptr;
   ba.B = B; ba.Hq = Hq; ba.Hkv = Hkv; ba.N = N; ba.d = d;
   ba.mode = mode; ba.k_win = k_win; ba.pi = pi; ba.M = M; ba.seg = seg;
   ba.m_min = skips ? (int)skip_m_min(k_win, pi) : 1;

@@ -24,7 +24,7 @@
 //   bwd_prep_kernel   D_i and c_i = log2(prior of local keys) - lse_i*log2(e)
 //   skip_bwd_kv_kernel / skip_bwd_q_kernel   (pi-Attention with skip keys)
 //       the skip-key contributions to dk, dv (key-owned) and dq, dalpha
-//       (query-owned), fp32, written to the workspace; 16x16 MFMA tiles over
+//       (query-owned), bf16, written to the workspace; 16x16 MFMA tiles over
 //       the residue chains i mod pi (one kernel when every chain is one tile)
 //   bwd_dq_kernel     query-stationary over the window / ECP keys: the
 //       forward's tile walk with S^T = K Q^T and dP^T = V dO^T on the matrix
@@ -53,7 +53,7 @@ struct Params {
   bf16 *dq, *dk, *dv;
   float *dalpha;
   float *Dv, *cv;                       // [B*Hq*N]
-  float *dq_s, *dk_s, *dv_s;            // skip contributions (nullptr without skips)
+  bf16 *dq_s, *dk_s, *dv_s;             // skip contributions, bf16 (nullptr without skips)
   int B, Hq, Hkv, N, mode, k_win, pi, M, m_min, seg, grp;
   int nqb, nkb;
   // skip-key residue chains: periods per residue, first position with a skip
@@ -131,6 +131,16 @@ template <int LD>
 __device__ __forceinline__ bf16x4 lds_tr16(const bf16 *rows, int c0, int G, int t) {
   const bf16 *src = rows + (4 * G + (t >> 2)) * LD + c0 + 4 * (t & 3);
   return as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src));
+}
+
+// Four fp32 values rounded to bf16 and stored as 8 bytes.
+__device__ __forceinline__ void store_bf16x4(bf16 *dst, f32x4 x) {
+  ushort4 u;
+  u.x = f32_to_bf16_bits(x[0]);
+  u.y = f32_to_bf16_bits(x[1]);
+  u.z = f32_to_bf16_bits(x[2]);
+  u.w = f32_to_bf16_bits(x[3]);
+  *(ushort4 *)dst = u;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -259,9 +269,9 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
         for (int db = 0; db < ND; ++db)
           aq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(ks, 16 * db, G, t), dsb, f32x4{}, 0, 0, 0);
         if (qvalid) {
-          float *dst = p.dq_s + qrow * D;
+          bf16 *dst = p.dq_s + qrow * D;
 #pragma unroll
-          for (int db = 0; db < ND; ++db) *(f32x4 *)(dst + 16 * db + 4 * G) = aq[db] * p.scale;
+          for (int db = 0; db < ND; ++db) store_bf16x4(dst + 16 * db + 4 * G, aq[db] * p.scale);
           if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
         }
       }
@@ -271,8 +281,8 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   const size_t krow = (size_t)bg * N + ik;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
-    *(f32x4 *)(p.dk_s + krow * D + 16 * db + 4 * G) = adk[db] * p.scale;
-    *(f32x4 *)(p.dv_s + krow * D + 16 * db + 4 * G) = adv[db];
+    store_bf16x4(p.dk_s + krow * D + 16 * db + 4 * G, adk[db] * p.scale);
+    store_bf16x4(p.dv_s + krow * D + 16 * db + 4 * G, adv[db]);
   }
 }
 
@@ -351,15 +361,15 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   da += wave_shfl_xor(da, 32);
   if (!qvalid) return;
 #pragma unroll
-  for (int db = 0; db < ND; ++db) *(f32x4 *)(p.dq_s + qrow * D + 16 * db + 4 * G) = aq[db] * p.scale;
+  for (int db = 0; db < ND; ++db) store_bf16x4(p.dq_s + qrow * D + 16 * db + 4 * G, aq[db] * p.scale);
   if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
 }
 
 // Store 16 accumulator values of a 32x32 C tile (rows 8(j/4) + 4h + j%4 of the
-// 32-row block db, column = this lane) as bf16, scaled, plus an fp32 seed.
+// 32-row block db, column = this lane) as bf16, scaled, plus a bf16 seed.
 template <int D>
 __device__ __forceinline__ void store_rows_bf16(bf16 *dst, const f32x16 (&acc)[D / 32], float scale,
-                                                const float *seed, int h) {
+                                                const bf16 *seed, int h) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -369,9 +379,11 @@ __device__ __forceinline__ void store_rows_bf16(bf16 *dst, const f32x16 (&acc)[D
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * scale;
       if (seed != nullptr) {
-        const f32x4 sd = *(const f32x4 *)(seed + dim);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] += sd[e];
+        const ushort4 sd = *(const ushort4 *)(seed + dim);
+        x[0] += bf16_to_f32(sd.x);
+        x[1] += bf16_to_f32(sd.y);
+        x[2] += bf16_to_f32(sd.z);
+        x[3] += bf16_to_f32(sd.w);
       }
       ushort4 u;
       u.x = f32_to_bf16_bits(x[0]);
@@ -696,7 +708,8 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
   p.q = (const bf16 *)a.q; p.k = (const bf16 *)a.k; p.v = (const bf16 *)a.v; p.o = (const bf16 *)a.o;
   p.dO = (const bf16 *)a.dO; p.alpha = a.alpha; p.lse = a.lse;
   p.dq = (bf16 *)a.dq; p.dk = (bf16 *)a.dk; p.dv = (bf16 *)a.dv; p.dalpha = a.dalpha;
-  p.Dv = a.Dv; p.cv = a.cv; p.dq_s = a.dq_s; p.dk_s = a.dk_s; p.dv_s = a.dv_s;
+  p.Dv = a.Dv; p.cv = a.cv;
+  p.dq_s = (bf16 *)a.dq_s; p.dk_s = (bf16 *)a.dk_s; p.dv_s = (bf16 *)a.dv_s;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.mode = a.mode; p.k_win = a.k_win; p.pi = a.pi;
   p.M = a.M; p.m_min = a.m_min; p.seg = a.seg; p.grp = a.Hq / a.Hkv;
   p.nqb = (a.N + BM - 1) / BM;
