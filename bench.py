@@ -492,8 +492,17 @@ def main():
     value = flop_step / (wall / args.steps) / 1e12
 
     # Dominant kernel: per-launch durations from HIP events on the launch stream.
-    t_ev = event_times(torch, step, args.steps)
-    kern_ms = float(np.mean(t_ev)) / (w.loops if w.loops > 1 else 1)
+    # One event pair around K back-to-back steps on the launch stream: the
+    # average launch duration as a kernel trace measures it (per-call event
+    # pairs add their own gaps to every launch).
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(st)
+    for _ in range(args.steps):
+        step()
+    ev1.record(st)
+    torch.cuda.synchronize()
+    kern_ms = ev0.elapsed_time(ev1) / args.steps / (w.loops if w.loops > 1 else 1)
     dominant = "prefill_bf16_kernel<%d>" % w.d
     achieved = flop / (kern_ms * 1e-3) / 1e12
     ai = flop / nb
