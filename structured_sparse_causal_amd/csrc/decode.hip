@@ -40,6 +40,7 @@ struct Params {
   int R, page_shift, num_pages, max_pages;   // ring / paged cache layouts
   const int *table;
   FusedOpts opt;    // bf16: score scale, cosine, query-driven gate, output gate
+  int walk_splits;  // bf16: one workgroup walks every split and writes o (no combine)
 };
 
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e)); }
@@ -366,7 +367,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = lane >> 4, t = lane & 15;
-  const int split = blockIdx.x;
+  // One split per workgroup, or (walk_splits) every split in turn with the
+  // running softmax state carried across them.
+  const int split = p.walk_splits ? 0 : blockIdx.x;
   const int g = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
   const int b = blockIdx.z;
   const int len = p.lens[b];
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   SplitRows sr = split_rows(p, i, split);
   if (!len_ok) sr.count = 0;
   bool bad_page;
-  const RowMap<LAYOUT> rm = make_rowmap<LAYOUT>(p, sr, b, g, lane, bad_page);
+  RowMap<LAYOUT> rm = make_rowmap<LAYOUT>(p, sr, b, g, lane, bad_page);
   if (bad_page) {   // an unmapped page: NaN output, no cache access
     len_ok = false;
     sr.count = 0;
@@ -548,11 +551,25 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
     }
   }
 
-  for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
+  const int nwalk = p.walk_splits ? p.nsplit : 1;
+  for (int sidx = 0; sidx < nwalk; ++sidx) {
+    if (sidx > 0) {   // next split of the walk: its rows, row map and first group
+      sr = split_rows(p, i, sidx);
+      if (!len_ok) sr.count = 0;
+      rm = make_rowmap<LAYOUT>(p, sr, b, g, lane, bad_page);
+      if (bad_page) {
+        len_ok = false;
+        sr.count = 0;
+      }
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-      ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, rm, r0 + (j + kRing - 1) * kStep, lane, fallback);
-      if (r0 + j * kStep < sr.count) consume(ring[j], r0 + j * kStep);
+      for (int j = 0; j + 1 < kRing; ++j) ring[j] = load_group<D>(Kp, Vp, rm, 16 * wave + j * kStep, lane, fallback);
+    }
+    for (int r0 = 16 * wave; r0 < sr.count; r0 += kRing * kStep) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        ring[(j + kRing - 1) % kRing] = load_group<D>(Kp, Vp, rm, r0 + (j + kRing - 1) * kStep, lane, fallback);
+        if (r0 + j * kStep < sr.count) consume(ring[j], r0 + j * kStep);
+      }
     }
   }
 
@@ -606,6 +623,27 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   __syncthreads();
   if (wave != 0) return;
   absorb(0);
+  if (p.walk_splits) {   // every split done: normalise, gate and write o
+#pragma unroll
+    for (int c4 = 0; c4 < HC4; ++c4)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int hd = 16 * hc + 4 * c4 + ii;
+        if (hd >= p.grp) continue;
+        const size_t row = (size_t)b * p.Hq + g * p.grp + hd;
+        const float inv = len_ok ? 1.0f / l_h[4 * c4 + ii] : NAN;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          float o = acc[c4][hh][ii] * inv;
+          if (p.opt.out_gate != nullptr) {
+            const unsigned short gu = ((const unsigned short *)p.opt.out_gate)[row * D + lane + 64 * hh];
+            o *= sigmoid_fast(bf16_to_f32(gu));
+          }
+          ((unsigned short *)p.o)[row * D + lane + 64 * hh] = f32_to_bf16_bits(o);
+        }
+      }
+    return;
+  }
   // ---- write this split's partial state: lane l holds dims l + 64hh ------------
 #pragma unroll
   for (int c4 = 0; c4 < HC4; ++c4)
@@ -655,6 +693,19 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(Params p) {
   else *op = o;
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <typename T, int D>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   Params p;
@@ -667,7 +718,18 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   p.opt = a.opt;
   p.scale_log2 = kLog2e * (a.opt.score_scale > 0.f ? a.opt.score_scale : 1.0f / sqrtf((float)D));
   p.R = a.R; p.page_shift = a.page_shift; p.num_pages = a.num_pages; p.max_pages = a.max_pages; p.table = a.table;
-  const dim3 grid(p.nsplit, a.Hkv * p.hchunks, a.B);
+  // Each (sequence, KV head, head chunk) workgroup walks all of its splits and
+  // writes o itself when those workgroups fill at least three quarters of the
+  // compute units in their last round (one workgroup then streams its rows
+  // at a fraction of a CU's bandwidth, so a round that leaves many CUs idle
+  // loses to the split plan).  Otherwise: one workgroup per split, and the
+  // combine kernel merges them.
+  p.walk_splits = 0;
+  if constexpr (sizeof(T) == 2) {
+    const long long wgs = (long long)a.B * a.Hkv * p.hchunks, cus = cu_count();
+    p.walk_splits = 4 * wgs >= 3 * cus * ((wgs + cus - 1) / cus);
+  }
+  const dim3 grid(p.walk_splits ? 1 : p.nsplit, a.Hkv * p.hchunks, a.B);
   if constexpr (sizeof(T) == 2) {
     const int heads = p.grp < 16 ? p.grp : 16;   // heads per workgroup
     const int hc4 = heads <= 4 ? 1 : heads <= 8 ? 2 : 4;
@@ -688,7 +750,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.walk_splits) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(D), 0, s, p);
   return hipGetLastError();
 }
