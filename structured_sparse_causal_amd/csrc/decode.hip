@@ -82,6 +82,20 @@ __device__ __forceinline__ SplitRows split_rows(const Params &p, int i, int spli
   return sr;
 }
 
+// All window rows below i as one split (the union of the window splits, in the
+// same order).  The window splits are multiples of 64 rows, so a wave taking
+// every fourth 16-row group meets the same rows in the same order either way.
+__device__ __forceinline__ SplitRows window_rows(const Params &p, int i) {
+  SplitRows sr;
+  const int lo = key_lo(i, p.mode, p.k_win, p.seg);
+  sr.qrow = i;
+  sr.count = i > lo ? i - lo : 0;
+  sr.base = lo;
+  sr.step = 1;
+  sr.last = false;
+  return sr;
+}
+
 // Physical row (relative to the per-layout base pointer) of row r of a split.
 //   contiguous [B,Hkv,Lmax,d]: base = (b,g) slice, row = position;
 //   ring [B,Hkv,R,d]: base = (b,g) slice, row = position mod R (a split's rows
@@ -368,8 +382,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = lane >> 4, t = lane & 15;
   // One split per workgroup, or (walk_splits) every split in turn with the
-  // running softmax state carried across them.
+  // running softmax state carried across them.  Contiguous and ring caches walk
+  // the window rows as one split (a paged split's pages must fit one table
+  // entry per lane).
   const int split = p.walk_splits ? 0 : blockIdx.x;
+  const bool merged = p.walk_splits && LAYOUT != kCachePaged;
   const int g = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
   const int b = blockIdx.z;
   const int len = p.lens[b];
@@ -385,7 +402,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
   const bf16 *Vp = (const bf16 *)p.vc + kvoff;
   const bf16 *Qp = (const bf16 *)p.q + ((size_t)b * p.Hq + hq) * D;
 
-  SplitRows sr = split_rows(p, i, split);
+  SplitRows sr = merged ? window_rows(p, i) : split_rows(p, i, split);
   if (!len_ok) sr.count = 0;
   bool bad_page;
   RowMap<LAYOUT> rm = make_rowmap<LAYOUT>(p, sr, b, g, lane, bad_page);
@@ -551,10 +568,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
     }
   }
 
-  const int nwalk = p.walk_splits ? p.nsplit : 1;
+  const int nwalk = merged ? 2 : p.walk_splits ? p.nsplit : 1;
   for (int sidx = 0; sidx < nwalk; ++sidx) {
     if (sidx > 0) {   // next split of the walk: its rows, row map and first group
-      sr = split_rows(p, i, sidx);
+      sr = split_rows(p, i, merged ? p.n_wsplit : sidx);
       if (!len_ok) sr.count = 0;
       rm = make_rowmap<LAYOUT>(p, sr, b, g, lane, bad_page);
       if (bad_page) {
