@@ -407,8 +407,8 @@ def cpu_baseline(w, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="ecp_bf16")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -494,9 +494,21 @@ def main():
     # Dominant kernel: per-launch durations from HIP events on the launch stream.
     # One event pair around K back-to-back steps on the launch stream: the
     # average launch duration as a kernel trace measures it (per-call event
-    # pairs add their own gaps to every launch).
+    # pairs add their own gaps to every launch).  Before it, the event pair is
+    # exercised once and the kernel runs for ~0.3 s untimed: the first timed
+    # event pair of a process and a GPU still raising its clock after an idle
+    # host phase both read up to ~15 % slow.
     st = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(st)
+    step()
+    ev1.record(st)
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.3:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     ev0.record(st)
     for _ in range(args.steps):
         step()

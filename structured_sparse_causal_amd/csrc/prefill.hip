@@ -37,6 +37,9 @@ namespace {
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
 constexpr float kTau = 8.0f;
+// Largest lane sum of one tile's probabilities accepted without taking the
+// row max (bf16 kernel): every probability is then at most 2^8.
+constexpr float kSumCap = 256.0f;
 
 struct Params {
   const void *q, *k, *v;
@@ -313,19 +316,32 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int ntiles = (hi_wg - t_begin) / BN + 1;
 
   // ---- direct-to-LDS staging of one K and one V tile -----------------------
+  // Lane L of DMA u carries 16 bytes of one tile row; the tile's first row j0
+  // goes into the scalar address, so a tile lying wholly below N costs no
+  // vector instructions (rows past N, in the last tile only, are clamped to
+  // N - 1: masked or probability 0).
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  unsigned soff[PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int pch = 64 * (PER_WAVE * wave + u) + lane;   // chunk position in LDS
+    const int row = pch / CPR;
+    soff[u] = (unsigned)(row * RB + (((pch % CPR) ^ tile_swz<D>(row)) << 4));
+  }
   auto stage = [&](int j0, int buf) __attribute__((always_inline)) {
+    const bf16 *kb = Kp + (size_t)j0 * D, *vb = Vp + (size_t)j0 * D;
+    const bool whole = j0 + BN <= N;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      const int slot = PER_WAVE * wave + u;             // 1 KB slot of the tile
-      const int pch = 64 * slot + lane;                 // chunk position in LDS
-      const int row = pch / CPR;
-      const int src = (pch % CPR) ^ tile_swz<D>(row);   // chunk held there
-      const int key = min(j0 + row, N - 1);             // rows past N: masked / probability 0
-      const unsigned voff = (unsigned)((key * D + src * 8) * 2);
-      const unsigned kdst = __builtin_amdgcn_readfirstlane(lds0 + buf * TILE + 1024 * slot);
-      dma16(Kp, voff, kdst);
-      dma16(Vp, voff, kdst + 2 * TILE);
+      unsigned off = soff[u];
+      if (!whole) {
+        const int row = (int)(off / RB);
+        off += (unsigned)((min(j0 + row, N - 1) - j0 - row) * RB);
+      }
+      const unsigned kdst = lds0 + buf * TILE + 1024 * (PER_WAVE * wave_s + u);
+      dma16(kb, off, kdst);
+      dma16(vb, off, kdst + 2 * TILE);
     }
   };
   // The first tile's loads go out before the query's, so the workgroup waits
@@ -429,87 +445,145 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Probabilities of a tile are exp2(s * sl2 + bias - m_run) against the
+  // running reference m_run (log2 units), rounded to bf16 for the P V
+  // product; the row sum adds the same rounded values (v_dot2_f32_bf16 with
+  // ones), so numerator and denominator use identical weights.  The first
+  // tile a wave computes takes the row max and sets m_run; later tiles skip
+  // the max and check instead that each lane's sum of probabilities stays
+  // <= 2^8 (so every probability does): only where it does not are the
+  // scores recomputed and the max taken, moving m_run up to it.  Either way
+  // every probability is at most 2^8 and the result is the same softmax.
+  bool fresh = true;   // no tile computed yet by this wave (wave-uniform)
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+  auto tile = [&](int t, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int j0 = t_begin + t * BN;
-    const int buf = t & 1;
     const bool more = t + 1 < ntiles;
     if (more) stage(j0 + BN, buf ^ 1);   // lands during the compute below
 
     if (wave_live && j0 <= w_hi && j0 + BN - 1 >= w_lo) {
       const char *KB = smem + buf * TILE;
       const char *VB = smem + (2 + buf) * TILE;
-      // ---- S^T = K Q^T for the 64-key tile: two 32x32 blocks -------------------
+      // mask cases (wave-uniform): keys above some row's hi / below some row's lo
+      const bool hi_part = !w_allvalid || j0 + BN - 1 > w_hi_first;
+      const bool lo_part = !w_allvalid || j0 < w_lo_last;
       f32x16 s[2];
+      // ---- S^T = K Q^T for the 64-key tile (two 32x32 blocks), masked --------
+      auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NQF; ++kk) {
-          const bf16x8 a = *(const bf16x8 *)(KB + 32 * kb * RB + koff[kk]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-        }
-      }
-
-      // ---- mask: key j visible to query i iff lo(i) <= j <= hi(i) --------------
-      const bool full = w_allvalid && (j0 + BN - 1 <= w_hi_first) && (j0 >= w_lo_last);
-      if (!full) {
-        // tile-local index of register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4
-        const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) {
-            const int off = 32 * kb + 8 * (jj >> 2) + (jj & 3);
-            if ((unsigned)(off - a0) > (unsigned)span) s[kb][jj] = -INFINITY;
+          for (int kk = 0; kk < NQF; ++kk) {
+            const bf16x8 a = *(const bf16x8 *)(KB + 32 * kb * RB + koff[kk]);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
           }
-      }
-
-      // ---- online softmax (log2 units, lazy rescale) ---------------------------
-      float mx = s[0][0];
-#pragma unroll
-      for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s[0][jj]);
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[1][jj]);
-      mx = half_swap_max(mx);
-      const float m_new = mx * sl2 + bias;
-      if (__any(m_new > m_run + kTau)) {
-        const float mr = fmaxf(m_run, m_new);
-        const float f = fast_exp2(m_run - mr);
-        l_run *= f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] *= f;
-        m_run = mr;
-      }
-      const float nb = bias - m_run;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float pv = fast_exp2(fmaf(s[kb][jj], sl2, nb));
-          s[kb][jj] = pv;
-          lsum += pv;
         }
+        // key j visible to query i iff lo(i) <= j <= hi(i); tile-local index
+        // of register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4
+        if (hi_part && lo_part) {
+          const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+              const int off = 32 * kb + 8 * (jj >> 2) + (jj & 3);
+              if ((unsigned)(off - a0) > (unsigned)span) s[kb][jj] = -INFINITY;
+            }
+        } else if (hi_part) {
+          const int th = hi_i - j0 - 4 * h;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+              if (32 * kb + 8 * (jj >> 2) + (jj & 3) > th) s[kb][jj] = -INFINITY;
+        } else if (lo_part) {
+          const int tl = lo_i - j0 - 4 * h;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+              if (32 * kb + 8 * (jj >> 2) + (jj & 3) < tl) s[kb][jj] = -INFINITY;
+        }
+      };
+      bf16x8 pb[4];
+      float lsum;
+      auto probs = [&](float nb) __attribute__((always_inline)) {
+        lsum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e], sl2, nb));
+            const float p1 = fast_exp2(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e + 1], sl2, nb));
+            const bf16x2 pr = {(bf16)p0, (bf16)p1};
+            w[e] = __builtin_bit_cast(unsigned, pr);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          }
+          pb[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+      };
+
+      // Row max, m_run moved up to it, probabilities against it.
+      auto with_max = [&]() __attribute__((always_inline)) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s[0][jj]);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[1][jj]);
+        mx = half_swap_max(mx);
+        const float m_new = mx * sl2 + bias;
+        if (__any(m_new > m_run)) {
+          const float mr = fmaxf(m_run, m_new);
+          const float f = fast_exp2(m_run - mr);
+          l_run *= f;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] *= f;
+          m_run = mr;
+        }
+        probs(bias - m_run);
+      };
+
+      scores();
+      if (fresh) {
+        with_max();
+        fresh = false;
+      } else {
+        probs(bias - m_run);
+        if (__any(!(lsum <= kSumCap))) {
+          // The probabilities replaced the scores: recompute them from the
+          // tile still in LDS (the empty asm makes the compiler re-read it
+          // rather than hold the first reads' fragments in registers).
+          asm volatile("" ::: "memory");
+          scores();
+          with_max();
+        }
+      }
       l_run += lsum;
 
       // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[kk >> 1][8 * (kk & 1) + e];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const char *base = VB + 16 * kk * RB;
           const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(base + voffs[db][0]));
           const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(base + voffs[db][1]));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(lo, hi), pb, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(lo, hi), pb[kk], acc[db], 0, 0, 0);
         }
       }
     }
 
     if (more) wait_dma();
     __syncthreads();
+  };
+  // Two tiles per trip, so each copy's LDS buffer offsets are constants.
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = acc / l ---------------------------------------------
