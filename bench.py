@@ -167,6 +167,19 @@ def event_times(torch, fn, reps):
     return np.array([a.elapsed_time(b) for a, b in evs])
 
 
+def warm(torch, fn, calls, seconds=0.15):
+    """Untimed calls: at least ``calls``, and until ``seconds`` of GPU work have
+    passed, so the clock has risen before anything is timed."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < calls or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def run_prefill_workload(torch, sa, w, reps, warmup):
     from structured_sparse_causal_amd.inputs import prefill_inputs
     dev = torch.device("cuda:0")
@@ -182,9 +195,7 @@ def run_prefill_workload(torch, sa, w, reps, warmup):
     else:
         def fn():
             sa.fwd(q, k, v, a, out=outs[0], workspace=ws, **prm)
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     t = event_times(torch, fn, reps)
     flop, nb = prefill_useful(w)
     flop *= w.loops
@@ -216,9 +227,7 @@ def run_decode_workload(torch, sa, w, reps, warmup):
     def fn():
         sa.decode(q, kc, vc, lens, a, mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg,
                   out=out, workspace=ws)
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     t = event_times(torch, fn, reps)
     flop, nb = decode_useful(w)
     ms = float(np.median(t))
@@ -246,9 +255,7 @@ def run_decode_layouts(torch, sa, w, reps, warmup):
     res = {}
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm(torch, fn, warmup)
         t = event_times(torch, fn, reps)
         ms = float(np.median(t))
         return {"ms": ms, "useful_GBps": nb / (ms * 1e-3) / 1e9,
@@ -295,9 +302,7 @@ def run_option_workloads(torch, sa, reps, warmup):
     res = {}
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm(torch, fn, warmup)
         return float(np.median(event_times(torch, fn, reps)))
 
     gen = torch.Generator(device="cpu")
@@ -360,9 +365,7 @@ def run_bwd_workload(torch, sa, w, reps, warmup):
 
     def fn():
         sa.bwd(q, k, v, a, o, lse, dO, workspace=ws, **prm)
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm(torch, fn, warmup)
     t = event_times(torch, fn, reps)
     flop = 10.0 * w.d * pairs_per_head(w) * w.B * w.Hq
     ms = float(np.median(t))
