@@ -1,9 +1,9 @@
 // prefill.hip -- window / paired-half-segment attention forward for gfx950.
 //
 // One workgroup (4 waves) owns a block of 128 consecutive query rows of one
-// (batch, head); each wave owns 32 of them.  Key/value tiles of 64 rows stream
-// through LDS; the workgroup walks the tiles covering the union of its rows'
-// key ranges:
+// (batch, head); each wave owns 32 of them.  Key/value tiles (64 rows for
+// d = 64, 32 rows for d = 128) stream through LDS; the workgroup walks the
+// tiles covering the union of its rows' key ranges:
 //   window (pi-Attention section 2 item 1; LT2 section 2.1): [max(0,i-k), i]
 //   ECP (PAR block, ECP section 2):       [max(0,(floor(i/s)-1)*s), i]
 //   and the further masks (two-sided window, s-Split segments, ECP pair
@@ -286,11 +286,12 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
 }
 
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
+template <int D, int TBN>
+__global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_bf16_kernel(Params p) {
   constexpr int RB = D * 2;              // bytes per K/V row
   constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int TILE = BN * RB;          // bytes per K or V tile
+  constexpr int NKB = TBN / 32;          // 32-key blocks per key tile
+  constexpr int TILE = TBN * RB;         // bytes per K or V tile
   constexpr int PER_WAVE = TILE / 1024 / 4;  // DMA instructions per wave per tile
   constexpr int NQF = D / 16;            // k-steps of the 32x32x16 score product
   constexpr int NDB = D / 32;            // 32-dim blocks of O^T
@@ -312,8 +313,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 
   // ---- key-tile range ---------------------------------------------------
   const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
-  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
-  const int ntiles = (hi_wg - t_begin) / BN + 1;
+  const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / TBN) * TBN;
+  const int ntiles = (hi_wg - t_begin) / TBN + 1;
 
   // ---- direct-to-LDS staging of one K and one V tile -----------------------
   // Lane L of DMA u carries 16 bytes of one tile row; the tile's first row j0
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   }
   auto stage = [&](int j0, int buf) __attribute__((always_inline)) {
     const bf16 *kb = Kp + (size_t)j0 * D, *vb = Vp + (size_t)j0 * D;
-    const bool whole = j0 + BN <= N;
+    const bool whole = j0 + TBN <= N;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       unsigned off = soff[u];
@@ -459,21 +460,21 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 
   auto tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int j0 = t_begin + t * BN;
+    const int j0 = t_begin + t * TBN;
     const bool more = t + 1 < ntiles;
-    if (more) stage(j0 + BN, buf ^ 1);   // lands during the compute below
+    if (more) stage(j0 + TBN, buf ^ 1);   // lands during the compute below
 
-    if (wave_live && j0 <= w_hi && j0 + BN - 1 >= w_lo) {
+    if (wave_live && j0 <= w_hi && j0 + TBN - 1 >= w_lo) {
       const char *KB = smem + buf * TILE;
       const char *VB = smem + (2 + buf) * TILE;
       // mask cases (wave-uniform): keys above some row's hi / below some row's lo
-      const bool hi_part = !w_allvalid || j0 + BN - 1 > w_hi_first;
+      const bool hi_part = !w_allvalid || j0 + TBN - 1 > w_hi_first;
       const bool lo_part = !w_allvalid || j0 < w_lo_last;
-      f32x16 s[2];
-      // ---- S^T = K Q^T for the 64-key tile (two 32x32 blocks), masked --------
+      f32x16 s[NKB];
+      // ---- S^T = K Q^T for the key tile (one 32x32 block per 32 keys), masked ----
       auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
           s[kb] = f32x16{};
 #pragma unroll
           for (int kk = 0; kk < NQF; ++kk) {
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
         if (hi_part && lo_part) {
           const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
               const int off = 32 * kb + 8 * (jj >> 2) + (jj & 3);
@@ -495,25 +496,25 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
         } else if (hi_part) {
           const int th = hi_i - j0 - 4 * h;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj)
               if (32 * kb + 8 * (jj >> 2) + (jj & 3) > th) s[kb][jj] = -INFINITY;
         } else if (lo_part) {
           const int tl = lo_i - j0 - 4 * h;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj)
               if (32 * kb + 8 * (jj >> 2) + (jj & 3) < tl) s[kb][jj] = -INFINITY;
         }
       };
-      bf16x8 pb[4];
+      bf16x8 pb[2 * NKB];
       float lsum;
       auto probs = [&](float nb) __attribute__((always_inline)) {
         lsum = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2 * NKB; ++kk) {
           u32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -533,7 +534,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
         for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s[0][jj]);
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[1][jj]);
+        for (int kb = 1; kb < NKB; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
         mx = half_swap_max(mx);
         const float m_new = mx * sl2 + bias;
         if (__any(m_new > m_run)) {
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 
       // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 2 * NKB; ++kk) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const char *base = VB + 16 * kk * RB;
@@ -651,7 +654,10 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   }
   p.opt = a.opt;
   p.scale_log2 = kLog2e * (a.opt.score_scale > 0.f ? a.opt.score_scale : 1.0f / sqrtf((float)D));
-  if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
+  // d = 128 uses 32-key tiles: 167 VGPRs and 32 KB of LDS let three waves
+  // share each SIMD (64-key tiles: 212 VGPRs, 64 KB, two waves), which more
+  // than pays for the doubled per-tile overhead.
+  if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, D == 64 ? 64 : 32>), dim3(p.total), dim3(256), 0, s, p);
   else hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3(p.total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
