@@ -315,6 +315,22 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
   const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
   const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / TBN) * TBN;
   const int ntiles = (hi_wg - t_begin) / TBN + 1;
+  // Tile order.  Head-major windows start each block's walk at the tile
+  // whose global index is 0 mod ntiles and wrap around, so that workgroups
+  // running side by side (neighbouring blocks, ntiles equal) load the same
+  // key tile at the same step and share it in L2 instead of each fetching it
+  // at a different time.  Any order gives the same softmax (the masks are
+  // per tile).
+  int rot = 0;
+  if (p.heads_per_xcd <= 0) {
+    rot = (t_begin / TBN) % ntiles;
+    rot = rot == 0 ? 0 : ntiles - rot;
+  }
+  auto tile_row = [&](int t) __attribute__((always_inline)) {
+    int u = t + rot;
+    if (u >= ntiles) u -= ntiles;
+    return t_begin + u * TBN;
+  };
 
   // ---- direct-to-LDS staging of one K and one V tile -----------------------
   // Lane L of DMA u carries 16 bytes of one tile row; the tile's first row j0
@@ -347,7 +363,7 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
   };
   // The first tile's loads go out before the query's, so the workgroup waits
   // once for both.
-  stage(t_begin, 0);
+  stage(tile_row(0), 0);
 
   const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
   float bias = 0.f;  // log2 of the local prior
@@ -460,9 +476,9 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
 
   auto tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int j0 = t_begin + t * TBN;
+    const int j0 = tile_row(t);
     const bool more = t + 1 < ntiles;
-    if (more) stage(j0 + TBN, buf ^ 1);   // lands during the compute below
+    if (more) stage(tile_row(t + 1), buf ^ 1);   // lands during the compute below
 
     if (wave_live && j0 <= w_hi && j0 + TBN - 1 >= w_lo) {
       const char *KB = smem + buf * TILE;
