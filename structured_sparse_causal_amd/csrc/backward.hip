@@ -437,6 +437,26 @@ __device__ __forceinline__ void stage_tile(const bf16 *src, int j0, int last, un
 }
 
 // ---- dq and dalpha: query-stationary walk over the window / ECP keys ---------
+// Walk order of a block's ntiles tiles starting at tile row t_begin: for the
+// window masks (every interior block has the same ntiles) the walk starts at
+// the tile whose global index is 0 mod ntiles and wraps around, so blocks
+// running side by side load the same tile at the same step and share it in
+// L2.  Any order gives the same sums up to rounding (masks are per tile).
+struct TileWalk {
+  int t_begin, ntiles, rot;
+  __device__ TileWalk(int tb, int nt, int mode) : t_begin(tb), ntiles(nt), rot(0) {
+    if (mode == kModePi || mode == kModeWindow || mode == kModeWindowBidir) {
+      const int r = (tb / BN) % nt;
+      rot = r == 0 ? 0 : nt - r;
+    }
+  }
+  __device__ __forceinline__ int row(int t) const {
+    int u = t + rot;
+    if (u >= ntiles) u -= ntiles;
+    return t_begin + u * BN;
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   constexpr int RB = D * 2, TILE = BN * RB, NQF = D / 16, NDB = D / 32;
@@ -455,9 +475,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   const TileOffsets<D> off(lane);
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
   const int t_begin = (key_lo(i0, p.mode, p.k_win, p.seg) / BN) * BN;
+  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
+  const int ntiles = (hi_wg - t_begin) / BN + 1;
+  const TileWalk walk(t_begin, ntiles, p.mode);
   // The first K/V tile goes out before the query rows: one wait covers both.
-  stage_tile<D>(Kp, t_begin, N - 1, lds0, wave, lane);
-  stage_tile<D>(Vp, t_begin, N - 1, lds0 + 2 * TILE, wave, lane);
+  stage_tile<D>(Kp, walk.row(0), N - 1, lds0, wave, lane);
+  stage_tile<D>(Vp, walk.row(0), N - 1, lds0 + 2 * TILE, wave, lane);
 
   bf16x8 qf[NQF], df[NQF];
 #pragma unroll
@@ -472,8 +495,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   const int hi_i = key_hi(qi, N, p.mode, p.k_win, p.seg);
-  const int hi_wg = key_hi(min(i0 + BM - 1, N - 1), N, p.mode, p.k_win, p.seg);
-  const int ntiles = (hi_wg - t_begin) / BN + 1;
   const bool wave_live = q0 < N;
   const int w_hi = key_hi(min(q0 + 31, N - 1), N, p.mode, p.k_win, p.seg);
   const int w_hi_first = key_hi(min(q0, N - 1), N, p.mode, p.k_win, p.seg);
@@ -484,12 +505,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(0);   // query rows, row scalars and the first tile
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t_begin + t * BN;
+    const int j0 = walk.row(t);
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
     if (more) {
-      stage_tile<D>(Kp, j0 + BN, N - 1, lds0 + (buf ^ 1) * TILE, wave, lane);
-      stage_tile<D>(Vp, j0 + BN, N - 1, lds0 + (2 + (buf ^ 1)) * TILE, wave, lane);
+      stage_tile<D>(Kp, walk.row(t + 1), N - 1, lds0 + (buf ^ 1) * TILE, wave, lane);
+      stage_tile<D>(Vp, walk.row(t + 1), N - 1, lds0 + (2 + (buf ^ 1)) * TILE, wave, lane);
     }
     if (wave_live && j0 <= w_hi && j0 + BN - 1 >= w_lo) {
       const char *KB = smem + buf * TILE;
@@ -596,6 +617,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
   const int hi_q = last_query(min(k0 + BM - 1, N - 1), p);
   const int t_begin = (first_query(k0, p) / BN) * BN;
   const int ntiles = (hi_q - t_begin) / BN + 1;
+  const TileWalk walk(t_begin, ntiles, p.mode);
   const int wq_hi = last_query(kw_last, p);   // last query seeing this wave's keys
   const int w_lq_first = last_query(min(j_w, N - 1), p);   // last query seeing all of them
   const int w_fq_first = first_query(min(j_w, N - 1), p);  // first query seeing any of them
@@ -619,21 +641,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
     const size_t qbase = ((size_t)b * p.Hq + g * p.grp + hh) * N;
     const bf16 *Qp = p.q + qbase * D, *Op = p.dO + qbase * D;
     const float *Cp = p.cv + qbase, *Dp = p.Dv + qbase;
-    stage_tile<D>(Qp, t_begin, N - 1, lds0, wave, lane);
-    stage_tile<D>(Op, t_begin, N - 1, lds0 + 2 * TILE, wave, lane);
-    stage_vec(Cp, t_begin, lds0 + 4 * TILE);
-    stage_vec(Dp, t_begin, lds0 + 4 * TILE + 512);
+    stage_tile<D>(Qp, walk.row(0), N - 1, lds0, wave, lane);
+    stage_tile<D>(Op, walk.row(0), N - 1, lds0 + 2 * TILE, wave, lane);
+    stage_vec(Cp, walk.row(0), lds0 + 4 * TILE);
+    stage_vec(Dp, walk.row(0), lds0 + 4 * TILE + 512);
     wait_dma();
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-      const int i0 = t_begin + t * BN;
+      const int i0 = walk.row(t);
       const int buf = t & 1;
       const bool more = t + 1 < ntiles;
       if (more) {
-        stage_tile<D>(Qp, i0 + BN, N - 1, lds0 + (buf ^ 1) * TILE, wave, lane);
-        stage_tile<D>(Op, i0 + BN, N - 1, lds0 + (2 + (buf ^ 1)) * TILE, wave, lane);
-        stage_vec(Cp, i0 + BN, lds0 + 4 * TILE + 256 * (buf ^ 1));
-        stage_vec(Dp, i0 + BN, lds0 + 4 * TILE + 512 + 256 * (buf ^ 1));
+        const int i1 = walk.row(t + 1);
+        stage_tile<D>(Qp, i1, N - 1, lds0 + (buf ^ 1) * TILE, wave, lane);
+        stage_tile<D>(Op, i1, N - 1, lds0 + (2 + (buf ^ 1)) * TILE, wave, lane);
+        stage_vec(Cp, i1, lds0 + 4 * TILE + 256 * (buf ^ 1));
+        stage_vec(Dp, i1, lds0 + 4 * TILE + 512 + 256 * (buf ^ 1));
       }
       // this wave's keys [j_w, kw_last] are seen by queries [w_fq_first, wq_hi]
       if (wave_live && i0 + BN - 1 >= w_fq_first && i0 <= wq_hi) {
