@@ -585,8 +585,12 @@ __device__ __forceinline__ int last_query(int j, const Params &p) {
 // ---- dk and dv: key-stationary walk over the query tiles -------------------------
 // d = 128 holds K, V (64 VGPRs) and the dK, dV accumulators (128) per lane:
 // one wave per SIMD, with the 512-entry register budget that allows.
-template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p) {
+// PART 0 computes dK and dV together; at d = 128 that holds K, V and both
+// accumulators (one wave per SIMD), so the launch splits into a dV pass
+// (PART 1: S, P and dV^T += dO^T P; no V, no dP) and a dK pass (PART 2: S,
+// dP, dS and dK^T += Q^T dS), each of which fits two waves per SIMD.
+template <int D, int PART>
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(Params p) {
   constexpr int RB = D * 2, TILE = BN * RB, NQF = D / 16, NDB = D / 32;
   // Q0 Q1 dO0 dO1 tiles, then per-query c and D (two buffers of 64 floats each)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * 256];
@@ -600,11 +604,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
   const bool kvalid = kj < N;
   const size_t krow = (size_t)bg * N + (kvalid ? kj : 0);
 
+  constexpr bool want_dv = PART != 2, want_dk = PART != 1;
   bf16x8 kf[NQF], vf[NQF];
 #pragma unroll
   for (int kk = 0; kk < NQF; ++kk) {
     kf[kk] = kvalid ? *(const bf16x8 *)(p.k + krow * D + 16 * kk + 8 * h) : bf16x8{};
-    vf[kk] = kvalid ? *(const bf16x8 *)(p.v + krow * D + 16 * kk + 8 * h) : bf16x8{};
+    if (want_dk) vf[kk] = kvalid ? *(const bf16x8 *)(p.v + krow * D + 16 * kk + 8 * h) : bf16x8{};
   }
   f32x16 adk[NDB], adv[NDB];
 #pragma unroll
@@ -674,7 +679,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
             const bf16x8 qa = *(const bf16x8 *)(QB + 32 * qb2 * RB + off.row[kk]);
             const bf16x8 oa = *(const bf16x8 *)(OB + 32 * qb2 * RB + off.row[kk]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
+            if (want_dk) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
           }
           // element jj: query i0 + 32 qb2 + 8(jj/4) + 4h + jj%4, key kj
 #pragma unroll
@@ -688,7 +693,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
               float pr = fast_exp2(fmaf(s[jj], p.scale_log2, cvv[e]));
               if (!full && (unsigned)(i0 + ql + e - vis_lo) > vis_span) pr = 0.f;
               s[jj] = pr;
-              dp[jj] = pr * (dp[jj] - dvv[e]);
+              if (want_dk) dp[jj] = pr * (dp[jj] - dvv[e]);
             }
           }
           // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
@@ -698,18 +703,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
             bf16x8 pb, sb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              pb[e] = (bf16)s[8 * k2 + e];
-              sb[e] = (bf16)dp[8 * k2 + e];
+              if (want_dv) pb[e] = (bf16)s[8 * k2 + e];
+              if (want_dk) sb[e] = (bf16)dp[8 * k2 + e];
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
               const char *ob = OB + 16 * kk * RB, *qbp = QB + 16 * kk * RB;
-              const short4v olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][0]));
-              const short4v ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][1]));
-              const short4v qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][0]));
-              const short4v qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][1]));
-              adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(olo, ohi), pb, adv[db], 0, 0, 0);
-              adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(qlo, qhi), sb, adk[db], 0, 0, 0);
+              if (want_dv) {
+                const short4v olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][0]));
+                const short4v ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(ob + off.tr[db][1]));
+                adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(olo, ohi), pb, adv[db], 0, 0, 0);
+              }
+              if (want_dk) {
+                const short4v qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][0]));
+                const short4v qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(qbp + off.tr[db][1]));
+                adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(qlo, qhi), sb, adk[db], 0, 0, 0);
+              }
             }
           }
         }
@@ -721,8 +730,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(Params p)
   if (!kvalid) return;
   // keys at or above N - m_min * pi are no query's skip key: no seed
   const bool seeded = p.dk_s != nullptr && kj < N - p.skip_first;
-  store_rows_bf16<D>(p.dk + krow * D, adk, p.scale, seeded ? p.dk_s + krow * D : nullptr, h);
-  store_rows_bf16<D>(p.dv + krow * D, adv, 1.0f, seeded ? p.dv_s + krow * D : nullptr, h);
+  if (want_dk) store_rows_bf16<D>(p.dk + krow * D, adk, p.scale, seeded ? p.dk_s + krow * D : nullptr, h);
+  if (want_dv) store_rows_bf16<D>(p.dv + krow * D, adv, 1.0f, seeded ? p.dv_s + krow * D : nullptr, h);
 }
 
 template <int D>
@@ -764,7 +773,15 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
     }
   }
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.Hq * p.nqb), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+  // d = 64: one pass (252 VGPRs, two waves per SIMD; split passes measured
+  // 20 % slower there).  d = 128: the dV and dK passes (two waves each,
+  // against one for the joint kernel).
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 0>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 1>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
