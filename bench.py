@@ -518,7 +518,7 @@ def main():
     ev1.record(st)
     torch.cuda.synchronize()
     kern_ms = ev0.elapsed_time(ev1) / args.steps / (w.loops if w.loops > 1 else 1)
-    dominant = "prefill_bf16_kernel<%d>" % w.d
+    dominant = "prefill_bf16_kernel<%d, %d>" % (w.d, 64 if w.d == 64 else 32)   # <head dim, key-tile rows>
     achieved = flop / (kern_ms * 1e-3) / 1e12
     ai = flop / nb
     bound = "mfma" if ai * HBM_PEAK_GBS / 1000.0 >= MFMA_BF16_PEAK_TFLOPS else "hbm"
