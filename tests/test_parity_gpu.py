@@ -60,6 +60,10 @@ CASES = [
     Workload("ecp_d128_f32", "ecp", "f32", 1, 1, 1, 700, 128, seg=200, seed=33),
     Workload("ecp_seg1_bf16", "ecp", "bf16", 1, 1, 1, 130, 64, seg=1, seed=34),
     Workload("window_d128_bf16", "window", "bf16", 1, 2, 2, 3000, 128, k_win=300, seed=41),
+    # d = 128 bf16 ECP: heavy-first rank order (B*H a multiple of 8, whole
+    # half-segments of whole blocks) and the ragged general order
+    Workload("ecp_d128_rank_bf16", "ecp", "bf16", 2, 4, 4, 1024, 128, seg=256, scale_inputs=True, seed=35),
+    Workload("ecp_d128_ragged_bf16", "ecp", "bf16", 1, 3, 3, 1000, 128, seg=192, seed=36),
     Workload("window_dense_bf16", "window", "bf16", 1, 2, 2, 333, 64, k_win=5000, seed=42),
     Workload("window_gqa_bf16", "window", "bf16", 2, 4, 2, 640, 128, k_win=129, seed=43),
     Workload("window_tiny_n_bf16", "window", "bf16", 1, 1, 1, 1, 64, k_win=3, seed=44),
