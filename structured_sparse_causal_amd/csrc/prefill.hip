@@ -20,9 +20,11 @@
 // loads of tile t+1 are in flight, and one barrier per tile hands the buffers
 // over.  Without staging registers the d = 64 kernel fits 4 waves per SIMD.
 //
-// The softmax is online in log2 units with lazy rescaling (the running max
-// only moves when a tile raises it by more than 8, so exp2 arguments stay
-// <= 8): exact, since numerator and denominator use the same reference.
+// The softmax is online in log2 units against a lazily moved reference:
+// exact, since numerator and denominator use the same reference.  The fp32
+// kernel moves it when a tile raises the row max by more than 8; the bf16
+// kernel takes the max only on a wave's first tile and afterwards checks the
+// tile's probability sums instead (see the tile loop).
 // For pi-Attention the periodic skip keys are handled by a separate pass
 // (skip.hip) whose partial softmax state (max, sum, accumulator) seeds the
 // running state here: the union gets one softmax, as the page requires.
