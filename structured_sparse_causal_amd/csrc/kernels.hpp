@@ -10,7 +10,8 @@ namespace sa {
 enum { kModePi = 0, kModeWindow = 1, kModeEcp = 2, kModeWindowBidir = 3, kModeSsplit = 4, kModeEcpFull = 5 };
 enum { kF32 = 0, kBF16 = 1 };
 
-// Prefill: query block of 128 rows per workgroup, key tiles of 64 rows.
+// Prefill: query block of 128 rows per workgroup; key tiles of 64 rows (the
+// bf16 kernel at d = 128 uses 32-row tiles; see prefill.hip).
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
 
