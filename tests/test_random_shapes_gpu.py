@@ -6,7 +6,8 @@ multiples of the 128-row query blocks or the key tiles, windows and segments
 of any size (including wider than the sequence) and skip periods below and
 above the window.  Every output element is compared with the fp64 oracle.
 Twelve more (bf16) run the training forward and the backward and compare
-every gradient element with the oracle's fp64 chain rule.
+every gradient element with the oracle's fp64 chain rule, and twelve
+decode cases with ragged cache lengths compare every output element.
 """
 from __future__ import annotations
 
@@ -95,3 +96,36 @@ def test_random_shape_backward(w):
     assert_grad_close(dv.float().cpu().numpy(), rv, w.name + " dv")
     if w.mode == "pi":
         assert_grad_close(da.cpu().numpy(), ra, w.name + " dalpha")
+
+
+def _decode_cases(n=12, seed=8096):
+    rng = np.random.default_rng(seed)
+    out = []
+    for idx in range(n):
+        mode = ["pi", "window", "ecp", "ssplit"][idx % 4]
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 5))
+        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 3000))
+        out.append(Workload("rdec%02d_%s_d%d" % (idx, mode, d), mode, "bf16", int(rng.integers(1, 40)), hq, hkv, L,
+                            d, k_win=int(rng.integers(0, L + 50)), pi=int(rng.integers(1, max(2, L // 3 + 2))),
+                            M=int(rng.integers(0, 16)) if mode == "pi" else 0,
+                            seg=int(rng.integers(1, max(2, L // 2 + 64))), decode=True, seed=900 + idx))
+    return out
+
+
+@pytest.mark.parametrize("w", _decode_cases(), ids=lambda w: w.name)
+def test_random_shape_decode(w):
+    """Single-token decode with ragged cache lengths (1..L per sequence) on
+    random shapes; the batch sizes span both the split plan and the walk
+    schedule."""
+    from structured_sparse_causal_amd.inputs import decode_inputs
+    print("case %s" % (w,), flush=True)
+    q, kc, vc, lens, a = decode_inputs(w)
+    g = torch.Generator().manual_seed(w.seed)
+    lens = torch.randint(1, w.N + 1, (w.B,), generator=g, dtype=torch.int32)
+    prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
+    o = sa.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV), None if a is None else a.to(DEV), **prm)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, kc, vc, lens, a if w.mode == "pi" else None, **prm)
+    assert_close(o.float().cpu().numpy(), ref, "bf16", w.name)
