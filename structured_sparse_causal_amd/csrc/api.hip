@@ -173,32 +173,42 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
   if (rc != SA_OK) return rc;
   rc = check_opts(fo, mode);
   if (rc != SA_OK) return rc;
-  const size_t kh = khat_bytes(fo, B, Hkv, N, d, dtype);
-  {
-    const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype), nkv = (size_t)B * Hkv * N * d * elem_size(dtype);
-    if (fo.out_gate != nullptr && overlap(o, nq, fo.out_gate, nq)) return fail(SA_ERR_INVALID, "output overlaps out_gate");
-    if (kh > 0) {
-      if (workspace == nullptr || workspace_bytes < kh || !aligned(workspace, 256))
-        return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the forward workspace size");
-      if (overlap(workspace, kh, q, nq) || overlap(workspace, kh, k, nkv) || overlap(workspace, kh, v, nkv) ||
-          overlap(workspace, kh, o, nq))
-        return fail(SA_ERR_INVALID, "workspace overlaps a tensor");
-      hipError_t e = sa::launch_normalize_rows(k, workspace, (long long)B * Hkv * N, d, dtype, (hipStream_t)stream);
-      if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
-      k = workspace;   // scores read the normalised keys
-      workspace = (char *)workspace + kh;
-      workspace_bytes -= kh;
-    }
-  }
+  // Every check happens here, before the first launch: an error return leaves
+  // nothing enqueued.
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * N * d * es, nkv = (size_t)B * Hkv * N * d * es;
+  const size_t nl = (size_t)B * Hq * N * sizeof(float);
+  const size_t na = (mode == SA_MODE_PI && alpha != nullptr) ? nl : 0;
+  const size_t ng = fo.out_gate != nullptr ? nq : 0;
+  if (overlap(o, nq, fo.out_gate, ng)) return fail(SA_ERR_INVALID, "output overlaps out_gate");
   if (lse != nullptr) {
     if (!aligned(lse, 4)) return fail(SA_ERR_INVALID, "misaligned lse");
-    const size_t nq = (size_t)B * Hq * N * d * elem_size(dtype), nl = (size_t)B * Hq * N * sizeof(float);
-    if (overlap(lse, nl, q, nq) || overlap(lse, nl, o, nq) || overlap(lse, nl, k, (size_t)B * Hkv * N * d * elem_size(dtype)) ||
-        overlap(lse, nl, v, (size_t)B * Hkv * N * d * elem_size(dtype)) || overlap(lse, nl, alpha, alpha ? nl : 0))
+    if (overlap(lse, nl, q, nq) || overlap(lse, nl, o, nq) || overlap(lse, nl, k, nkv) || overlap(lse, nl, v, nkv) ||
+        overlap(lse, nl, alpha, na) || overlap(lse, nl, fo.out_gate, ng))
       return fail(SA_ERR_INVALID, "lse overlaps a tensor");
   }
+  // Workspace: [L2-normalised key copy (cosine scores)] [skip-key partial state (pi with skip keys)].
+  const size_t kh = khat_bytes(fo, B, Hkv, N, d, dtype);
   const bool skips = has_skips(mode, k_win, pi, M, N);
+  const int chunk = skips ? fwd_chunk_heads(B, Hq, Hkv, N, d, dtype) : 0;
+  const FwdLayout L = skips ? fwd_layout(chunk, N, d, dtype) : FwdLayout{0, 0, 0};
+  const size_t need = kh + L.total;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the forward workspace size");
+    if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nkv) || overlap(workspace, need, v, nkv) ||
+        overlap(workspace, need, o, nq) || overlap(workspace, need, alpha, na) ||
+        overlap(workspace, need, lse, lse != nullptr ? nl : 0) || overlap(workspace, need, fo.out_gate, ng))
+      return fail(SA_ERR_INVALID, "workspace overlaps a tensor");
+  }
   hipStream_t s = (hipStream_t)stream;
+  if (kh > 0) {
+    hipError_t e = sa::launch_normalize_rows(k, workspace, (long long)B * Hkv * N, d, dtype, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+    k = workspace;   // scores read the normalised keys
+    workspace = (char *)workspace + kh;
+  }
   sa::PrefillArgs pa;
   pa.q = q; pa.k = k; pa.v = v; pa.alpha = alpha; pa.o = o;
   pa.skip_ml = nullptr; pa.skip_acc = nullptr; pa.lse = lse;
@@ -211,14 +221,6 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
     return SA_OK;
   }
-  const int chunk = fwd_chunk_heads(B, Hq, Hkv, N, d, dtype);
-  const FwdLayout L = fwd_layout(chunk, N, d, dtype);
-  if (workspace == nullptr || workspace_bytes < L.total)
-    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than sparse_attn_fwd_workspace_size()");
-  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
-  const size_t es = elem_size(dtype);
-  const size_t nq = (size_t)B * Hq * N * d * es;
-  if (overlap(o, nq, workspace, L.total)) return fail(SA_ERR_INVALID, "output overlaps the workspace");
   const long long mm = skip_m_min(k_win, pi);
   const int grp = Hq / Hkv;
   const size_t head_elems = (size_t)N * d;
@@ -230,7 +232,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
     sk.q = (const char *)q + (size_t)bh0 * head_elems * es;
     sk.k = (const char *)k + (size_t)(bh0 / grp) * head_elems * es;
     sk.v = (const char *)v + (size_t)(bh0 / grp) * head_elems * es;
-    sk.alpha = alpha + (size_t)bh0 * N;
+    sk.alpha = alpha != nullptr ? alpha + (size_t)bh0 * N : nullptr;   // null with the query-driven gate
     sk.ml = (float *)((char *)workspace + L.ml_off);
     sk.acc = (char *)workspace + L.acc_off;
     sk.B = 1; sk.Hq = n; sk.Hkv = n / grp; sk.N = N; sk.d = d; sk.dtype = dtype;

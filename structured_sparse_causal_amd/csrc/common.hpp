@@ -143,17 +143,20 @@ __device__ __forceinline__ int tile_swz(int r) {
 // lds_base + 16 * L.  Issued through inline asm so that the compiler does not
 // wait for it before unrelated LDS reads; the caller waits (vmcnt) itself.
 __device__ __forceinline__ void dma16(const void *gbase, unsigned voff, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  // m0 (the LDS destination) is an operand bound to that register, so the
+  // compiler writes it and knows it changed; the s_nop covers the m0-write ->
+  // LDS-DMA hazard, which the compiler cannot see inside the asm.
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "v"(voff), "s"(gbase), "{m0}"(lds_base)
                : "memory");
 }
 
 // 4 bytes per lane to LDS address lds_base + 4 * lane.
 __device__ __forceinline__ void dma4(const void *gbase, unsigned voff, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
                :
-               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "v"(voff), "s"(gbase), "{m0}"(lds_base)
                : "memory");
 }
 

@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256, 2) void prefill_f32_kernel(Params p) {
 
   const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
   float bias = 0.f;  // log2 of the local prior
-  if (p.mode == kModePi && p.alpha != nullptr && qvalid) bias = __log2f(p.alpha[(size_t)bh * N + qi]);
+  if (p.mode == kModePi && p.alpha != nullptr && p.opt.gate_w == nullptr && qvalid)
+    bias = __log2f(p.alpha[(size_t)bh * N + qi]);
 
   float qf[D / 2];
 #pragma unroll
@@ -369,7 +370,8 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
 
   const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
   float bias = 0.f;  // log2 of the local prior
-  if (p.mode == kModePi && p.alpha != nullptr && qvalid) bias = __log2f(p.alpha[(size_t)bh * N + qi]);
+  if (p.mode == kModePi && p.alpha != nullptr && p.opt.gate_w == nullptr && qvalid)
+    bias = __log2f(p.alpha[(size_t)bh * N + qi]);
 
   bf16x8 qf[NQF];
 #pragma unroll

@@ -117,6 +117,24 @@ def test_fused_options_full_size_sampled():
     assert_close(o[rows], ref, "bf16", "pi query gate")
 
 
+def test_pi_query_gate_several_chunks_sampled():
+    # the query-driven gate with no alpha tensor, on a shape whose skip pass
+    # and prefill run over several chunks of head groups
+    w = WORKLOADS["pi_bf16"].replace(name="pi_gate_chunks", B=2, Hq=32, Hkv=8, N=32768, k_win=200, pi=700,
+                                     M=20, seed=71)
+    say("pi query gate over chunks %s" % (w,))
+    whole = w.B * w.Hq * w.N * (8 + 2 * w.d)
+    assert 0 < sa.fwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, torch.bfloat16, "pi", w.k_win, w.pi,
+                                    w.M) < whole / 2
+    gen = torch.Generator().manual_seed(98)
+    q, k, v, _ = prefill_inputs(w, device=DEV)
+    gw, gb = gate_params(w, gen)
+    o = sa.fwd(q, k, v, None, gate_w=gw.to(DEV), gate_b=gb.to(DEV), **prm(w)).float().cpu().numpy().reshape(-1, w.d)
+    rows = sample_rows(np.random.default_rng(12), w.B, w.Hq, w.N, 4000)
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), None, rows=rows, gate_w=gw, gate_b=gb, **prm(w))
+    assert_close(o[rows], ref, "bf16", "pi query gate, chunked")
+
+
 def test_decode_all_options_full_size():
     w = WORKLOADS["decode_pi_gqa_bf16"]
     say("full-size decode with every option")

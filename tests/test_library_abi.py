@@ -342,3 +342,20 @@ def test_bwd_ex_and_decode_ex_rejects(lib):
     dargs = (Q, K, V, A, A + 4096, O, 2, 8, 2, 512, 128)
     assert lib.sparse_attn_decode_ex(*dargs, F32, PI, 64, 64, 3, 0, opts(score_scale=0.1), WS, 1 << 30, None) == UNSUPPORTED
     assert lib.sparse_attn_decode_ex(*dargs, BF16, PI, 64, 64, 3, 0, opts(out_gate=O + 16), WS, 1 << 30, None) == INVALID
+
+
+def test_fwd_ex_checks_everything_before_the_first_launch(lib):
+    # Cosine scores with skip keys: the workspace holds the key copy and the
+    # skip state.  Too small for both must be reported before the key
+    # normalisation is launched (here no device exists: a launch attempt would
+    # come back as a HIP error instead of the workspace error).
+    kc = 256 * (-(-(2 * 256 * 64 * 2) // 256))   # the key copy alone
+    assert fwd_ex(lib, opts(cosine=1), mode=PI, ws=WS, wsb=kc) == WORKSPACE
+    # the lse, alpha and out_gate regions may not overlap the workspace either
+    LSE2 = WS + 4096
+    assert fwd_ex(lib, opts(cosine=1), mode=PI, lse=LSE2) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+    assert fwd_ex(lib, opts(cosine=1, out_gate=WS + 512), mode=PI) == INVALID
+    assert fwd_ex(lib, opts(cosine=1), mode=PI, a=WS + 1024) == INVALID
+    # an lse overlapping out_gate is rejected too
+    assert fwd_ex(lib, opts(out_gate=OG), lse=OG + 64) == INVALID
