@@ -2,15 +2,18 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One "step" is one forward of the headline workload (default: ECP
-paired-half-segment attention, bf16, B=4 H=12 N=4096 d=64 s=512) on synthetic
-inputs already resident in HBM.  ``value`` is useful TFLOP/s: 4*d FLOPs per
-attended (query, key) pair, nothing for masked or padded work.  The same JSON
-line carries the roofline of the dominant kernel (timed live with HIP events
-on the launch stream), the other workloads of the hot path (pi-Attention
-prefill, the looped window block, GQA decode), the backward pass of one layer
-call on the three prefill shapes, and the CPU oracle timed on a bounded sample
-of the headline workload.
+One "step" is one pass of the headline workload (default: the looped
+window-attention block, bf16, B=1 H=32 N=65536 d=128, window k=1024, applied
+4 times with each output fed back as the next V: the largest single-GPU
+configuration) on synthetic inputs already resident in HBM.  ``value`` is
+useful TFLOP/s: 4*d FLOPs per attended (query, key) pair, nothing for masked
+or padded work.  The same JSON line carries the roofline of the dominant
+kernel (timed live with HIP events on the launch stream), a cold-cache timing
+of the step, the other workloads of the hot path (ECP, pi-Attention prefill,
+the fp32 tiny case, GQA decode) each with its own roofline fraction and
+recorded HBM traffic, the backward pass of one layer call on the three
+prefill shapes, and the CPU oracle timed on a bounded sample of the headline
+workload.
 
 Only one GPU is used; ``--gpus N`` with N > 1 exits with a message.
 """
@@ -39,27 +42,41 @@ def log(*a):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("structured_sparse_causal_amd/csrc/prefill.hip",
-                  "structured_sparse_causal_amd/csrc/common.hpp")
+_CSRC = "structured_sparse_causal_amd/csrc/"
+# Sources whose kernels a workload's library call runs: a recorded counter
+# measurement is reused only while their hash is unchanged.
+_PREFILL_SOURCES = (_CSRC + "prefill.hip", _CSRC + "common.hpp", _CSRC + "kernels.hpp")
+KERNEL_SOURCES = {
+    "prefill": _PREFILL_SOURCES,
+    "pi": _PREFILL_SOURCES + (_CSRC + "skip.hip", _CSRC + "api.hip"),
+    "decode": (_CSRC + "decode.hip", _CSRC + "common.hpp", _CSRC + "kernels.hpp", _CSRC + "api.hip"),
+}
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the sources of the dominant (prefill) kernel: a recorded
-    counter measurement is only reused while this hash is unchanged."""
+def source_set(w) -> str:
+    if w.decode:
+        return "decode"
+    return "pi" if (w.mode == "pi" and w.M > 0) else "prefill"
+
+
+def kernel_source_hash(kind: str = "prefill") -> str:
+    """sha256 over the sources of the kernels one call of that kind runs."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel, from the rocprofv3 counter
-    summary committed under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
-    by the reading of a plain copy of known size).  None if there is no
-    summary for this workload or the kernel changed since it was taken."""
-    path = os.path.join(PROFILES, "counters_%s.md" % workload)
+def recorded_traffic(w, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes of the workload's dominant kernel per launch (or, with
+    key="hbm_bytes_per_call", of every kernel of one library call), from the
+    rocprofv3 counter summary committed under profiles/ (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the reading of a plain copy of known size).
+    None if there is no summary for this workload or its kernels changed
+    since it was taken."""
+    path = os.path.join(PROFILES, "counters_%s.md" % w.name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -68,12 +85,20 @@ def recorded_traffic(workload: str):
             if ":" in line and line.strip().startswith("- "):
                 k, v = line.strip()[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(source_set(w)):
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def dominant_kernel(w) -> str:
+    if w.decode:
+        return "decode_bf16_kernel<%d, ...>" % w.d
+    if w.dtype == "f32":
+        return "prefill_f32_kernel<%d>" % w.d
+    return "prefill_bf16_kernel<%d, %d>" % (w.d, 64 if w.d == 64 else 32)   # <head dim, key-tile rows>
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
@@ -211,8 +236,27 @@ def run_prefill_workload(torch, sa, w, reps, warmup):
         "pct_attainable": 100.0 * flop / (ms * 1e-3) / 1e12 / attainable,
         "useful_flop": flop, "useful_bytes": nb, "launches": w.loops * (2 if nbytes else 1),
     }
+    res.update(workload_roofline(w, flop, nb, ms / max(w.loops, 1)))
     del q, k, v, a, outs, ws
     return res
+
+
+def workload_roofline(w, flop, nb, ms_call):
+    """Roofline fraction of one library call of the workload (all its
+    kernels) and the HBM bytes recorded for that call under profiles/."""
+    per_call_flop, per_call_bytes = flop / max(w.loops, 1), nb / max(w.loops, 1)
+    if w.decode:
+        bound, frac = "hbm", per_call_bytes / (ms_call * 1e-3) / 1e9 / HBM_PEAK_GBS
+    elif w.dtype == "f32":
+        bound, frac = "mfma_f32", per_call_flop / (ms_call * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS
+    else:
+        attainable = min(MFMA_BF16_PEAK_TFLOPS, per_call_flop / per_call_bytes * HBM_PEAK_GBS / 1000.0)
+        bound = "mfma" if attainable >= MFMA_BF16_PEAK_TFLOPS else "hbm"
+        frac = per_call_flop / (ms_call * 1e-3) / 1e12 / attainable
+    t = recorded_traffic(w, "hbm_bytes_per_call")
+    return {"bound": bound, "frac": frac, "traffic": t,
+            "traffic_over_algorithmic": (t / per_call_bytes) if t is not None else None,
+            "dominant_kernel": dominant_kernel(w)}
 
 
 def run_decode_workload(torch, sa, w, reps, warmup):
@@ -237,6 +281,7 @@ def run_decode_workload(torch, sa, w, reps, warmup):
         "pct_hbm_peak": 100.0 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "tokens_per_s": w.B / (ms * 1e-3), "useful_bytes": nb, "useful_flop": flop,
     }
+    res.update(workload_roofline(w, flop, nb, ms))
     del q, kc, vc, lens, a, out, ws
     return res
 
@@ -403,8 +448,9 @@ def cpu_baseline(w, budget_s=12.0):
         dt = run(nh)
     flop = per_head_flop * nh
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
-            "sample": "%d of %d (batch, head) slices of %s, all %d query rows each, fp64 C oracle; "
-                      "%.2f s" % (nh, total, w.name, w.N, dt)}
+            "sample": "%d of %d (batch, head) slices of %s%s, all %d query rows each, fp64 C oracle; "
+                      "%.2f s" % (nh, total, w.name, " (its first application; the other %d apply the same "
+                                  "key sets)" % (w.loops - 1) if w.loops > 1 else "", w.N, dt)}
 
 
 def main():
@@ -412,7 +458,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--workload", default="ecp_bf16")
+    ap.add_argument("--workload", default="window_loop_bf16")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, metavar="WORKLOAD",
@@ -518,7 +564,7 @@ def main():
     ev1.record(st)
     torch.cuda.synchronize()
     kern_ms = ev0.elapsed_time(ev1) / args.steps / (w.loops if w.loops > 1 else 1)
-    dominant = "prefill_bf16_kernel<%d, %d>" % (w.d, 64 if w.d == 64 else 32)   # <head dim, key-tile rows>
+    dominant = dominant_kernel(w)
     achieved = flop / (kern_ms * 1e-3) / 1e12
     ai = flop / nb
     bound = "mfma" if ai * HBM_PEAK_GBS / 1000.0 >= MFMA_BF16_PEAK_TFLOPS else "hbm"
@@ -529,8 +575,8 @@ def main():
         gbs = nb / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS, "traffic": None}
-    traffic = recorded_traffic(w.name)
-    roof["traffic"] = traffic
+    roof["traffic"] = recorded_traffic(w)
+    roof["traffic_over_algorithmic"] = roof["traffic"] / nb if roof["traffic"] is not None else None
     roof["kernel"] = dominant
     roof["kernel_ms"] = kern_ms
     roof["algorithmic_flop_per_launch"] = flop
@@ -550,9 +596,12 @@ def main():
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
     cold_ms = float(np.median(cold))
+    cold_tf = flop_step / (cold_ms * 1e-3) / 1e12
     cold_rec = {"ms": cold_ms, "ms_p10": float(np.percentile(cold, 10)), "ms_p90": float(np.percentile(cold, 90)),
-                "useful_tflops": flop_step / (cold_ms * 1e-3) / 1e12, "steps": len(cold),
-                "note": "one step after a 1 GiB scratch write, per-step event pair"}
+                "useful_tflops": cold_tf, "pct_bf16_mfma_peak": 100.0 * cold_tf / MFMA_BF16_PEAK_TFLOPS,
+                "steps": len(cold), "warm_over_cold": value / cold_tf,
+                "note": "one step after a 1 GiB scratch write (inputs evicted from L2 and the 256 MB "
+                        "last-level cache), per-step event pair"}
     log("headline cold-cache: %.4f ms/step" % cold_ms)
     del q, k, v, a, out, outs, ws, scratch
     torch.cuda.empty_cache()
