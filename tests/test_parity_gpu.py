@@ -235,14 +235,15 @@ def _sample_rows(rng, B, H, N, n, hs=None):
 
 
 @pytest.mark.parametrize("name", ["ecp_bf16", "pi_bf16"])
-def test_full_size_sampled(name):
+def test_full_size_every_row(name):
+    # every output element of the full workload (about 35 GFLOP of fp64 work
+    # for the oracle, seconds on the host's cores)
     w = WORKLOADS[name]
-    say("full-size %s" % name)
+    say("full-size %s, every row" % name)
     q, k, v, a = prefill_inputs(w, device=DEV)
-    o = gpu_fwd(w, q, k, v, a).float().cpu().numpy().reshape(-1, w.d)
-    rows = _sample_rows(np.random.default_rng(5), w.B, w.Hq, w.N, 3000)
-    ref = oracle_fwd(w, q.cpu(), k.cpu(), v.cpu(), None if a is None else a.cpu(), rows=rows)
-    assert_close(o[rows], ref, "bf16", name)
+    o = gpu_fwd(w, q, k, v, a).float().cpu().numpy()
+    ref = oracle_fwd(w, q.cpu(), k.cpu(), v.cpu(), None if a is None else a.cpu())
+    assert_close(o, ref, "bf16", name)
 
 
 def test_pi_gqa_several_chunks_sampled():
@@ -268,12 +269,13 @@ def test_full_size_window_loop_sampled():
     q, k = qd.cpu(), kd.cpu()
     vin = vd
     rng = np.random.default_rng(6)
-    heads = [0, 17, 31]
+    heads = [0, 5, 9, 14, 17, 22, 27, 31]
     for t in range(w.loops):
         o = sa.fwd(qd, kd, vin, mode="window", k_win=w.k_win)
         torch.cuda.synchronize()
         for h in heads:
-            rows = np.concatenate([rng.integers(0, w.N, 200), [0, 1, w.N - 1, 1024, 1025]])
+            rows = np.concatenate([rng.integers(0, w.N, 1500), [0, 1, w.N - 1, 1024, 1025],
+                                   np.arange(1000, 1160)])
             ref = oracle.fwd(q[:, h:h + 1], k[:, h:h + 1], vin[:, h:h + 1].cpu(), mode="window",
                              k_win=w.k_win, rows=rows)
             got = o[0, h, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
@@ -281,14 +283,22 @@ def test_full_size_window_loop_sampled():
         vin = o
 
 
-def test_full_size_decode_sampled():
+def test_full_size_decode_every_sequence():
+    # all 64 sequences, with the benchmark's full caches and then with ragged
+    # lengths (including 1, the window edge and the skip edge); the oracle
+    # reads each sequence's cache slice from the host
     w = WORKLOADS["decode_pi_gqa_bf16"]
-    say("full-size %s" % w.name)
+    say("full-size %s, every sequence" % w.name)
     q, kc, vc, lens, a = decode_inputs(w, device=DEV)
-    o = sa.decode(q, kc, vc, lens, a, mode="pi", k_win=w.k_win, pi=w.pi, M=w.M)
-    torch.cuda.synchronize()
-    for b in (0, 31, 63):
-        ref = oracle.decode(q[b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(),
-                            lens[b:b + 1].cpu(), a[b:b + 1].cpu(), mode="pi", k_win=w.k_win,
-                            pi=w.pi, M=w.M)
-        assert_close(o[b:b + 1].float().cpu().numpy(), ref, "bf16", "decode seq %d" % b)
+    rng = np.random.default_rng(11)
+    ragged = rng.integers(1, w.N + 1, w.B)
+    ragged[:6] = [1, 2, w.k_win, w.k_win + 2, w.pi * 3 + 1, w.N]
+    prm = dict(mode="pi", k_win=w.k_win, pi=w.pi, M=w.M)
+    for tag, ln in (("full", lens), ("ragged", torch.from_numpy(ragged.astype(np.int32)).to(DEV))):
+        o = sa.decode(q, kc, vc, ln, a, **prm).float().cpu().numpy()
+        lnc = ln.cpu()
+        for b0 in range(0, w.B, 8):
+            say("  %s sequences %d..%d" % (tag, b0, b0 + 7))
+            sl = slice(b0, b0 + 8)
+            ref = oracle.decode(q[sl].cpu(), kc[sl].cpu(), vc[sl].cpu(), lnc[sl], a[sl].cpu(), **prm)
+            assert_close(o[sl], ref, "bf16", "decode %s seq %d..%d" % (tag, b0, b0 + 7))
