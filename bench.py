@@ -527,6 +527,18 @@ def main():
         else:
             sa.fwd(q, k, v, a, out=out, workspace=ws, **prm)
 
+    # Untimed clock settling (at least 0.3 s of steps: the engine clock rises
+    # over the first few hundred milliseconds of work), then the W warm-up
+    # steps, then the K timed steps.
+    settle_t0 = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - settle_t0 < 0.3:
+        step()
+        settle_steps += 1
+        if settle_steps % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle_s = time.perf_counter() - settle_t0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -666,6 +678,7 @@ def main():
                    "N": w.N, "d": w.d, "k_win": w.k_win, "pi": w.pi, "M": w.M, "seg": w.seg,
                    "loops": w.loops, "parallelism": "none (1 GPU)"},
         "pct_bf16_mfma_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
+        "clock_settle": {"untimed_steps": settle_steps, "seconds": settle_s},
         "roofline": roof,
         "cold_cache": cold_rec,
         "cpu_baseline": cpu,
