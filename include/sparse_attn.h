@@ -190,6 +190,30 @@ int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same operation, arguments and results as
+ * sparse_attn_decode over a contiguous cache, without the workspace
+ * arguments: the split partial states go to a device scratch array that the
+ * library holds for each GPU it runs on (16 MiB, kept until the process
+ * ends; its address is looked up on the first call on each device, with that
+ * device current).  The call allocates nothing.
+ *   Limit: sparse_attn_decode_workspace_size(...) of the same arguments must
+ *   not exceed sparse_attn_decode_noalloc_max_workspace() (16 MiB), else
+ *   SA_ERR_WORKSPACE and nothing is launched.
+ *   Every call on one GPU uses that GPU's one scratch array: calls that
+ *   overlap in time on the same GPU (different streams or threads without
+ *   ordering between them) race and give undefined results.  Calls ordered
+ *   on one stream are safe.  Nothing in the scratch needs clearing between
+ *   calls (every partial state a call reads was written by that call).
+ */
+size_t sparse_attn_decode_noalloc_max_workspace(void);
+int sparse_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                               const int *cache_lens, const float *alpha, void *o,
+                               int B, int Hq, int Hkv, int Lmax, int d, int dtype,
+                               int mode, int k_win, int pi, int M, int seg, void *stream);
+
+/*
  * Serving-cache layouts for the same decode (bf16 I/O only; fp32 returns
  * SA_ERR_UNSUPPORTED).  Semantics, q, alpha, o, cache_lens and workspace as
  * sparse_attn_decode; only where a position's key/value row lives differs.

@@ -61,6 +61,7 @@ EXPORTED = ("sparse_attn_fwd_workspace_size", "sparse_attn_fwd", "sparse_attn_fw
             "sparse_attn_decode_paged_workspace_size", "sparse_attn_decode_paged",
             "sparse_attn_fwd_ex_workspace_size", "sparse_attn_fwd_ex", "sparse_attn_decode_ex",
             "sparse_attn_bwd_ex_workspace_size", "sparse_attn_bwd_ex",
+            "sparse_attn_decode_noalloc_max_workspace", "sparse_attn_decode_noalloc",
             "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_version")
 
 
@@ -116,6 +117,10 @@ def load_library():
         lib.sparse_attn_decode_workspace_size.argtypes = [i] * 11
         lib.sparse_attn_decode.restype = i
         lib.sparse_attn_decode.argtypes = [vp] * 6 + [i] * 11 + [vp, sz, vp]
+        lib.sparse_attn_decode_noalloc_max_workspace.restype = sz
+        lib.sparse_attn_decode_noalloc_max_workspace.argtypes = []
+        lib.sparse_attn_decode_noalloc.restype = i
+        lib.sparse_attn_decode_noalloc.argtypes = [vp] * 6 + [i] * 11 + [vp]
         lib.sparse_attn_status_string.restype = ctypes.c_char_p
         lib.sparse_attn_status_string.argtypes = [i]
         lib.sparse_attn_last_error.restype = ctypes.c_char_p
@@ -339,6 +344,35 @@ def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0,
                                 nbytes if ws is not None else 0, _stream(q.device))
     if rc != SA_OK:
         _raise(lib, rc, "sparse_attn_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
+                   M: int = 0, seg: int = 0, out=None):
+    """The decode of ``decode`` through the allocation-free entry point: no
+    workspace (the library's per-GPU device scratch holds the partial
+    states).  With ``out`` given, this call allocates nothing either."""
+    lib = load_library()
+    _need_gpu(q, k_cache, v_cache, cache_lens, alpha, out)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and caches [B, Hkv, Lmax, d]")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise NotImplementedError("q and caches must share dtype bf16 or fp32")
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Lmax, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    if alpha is not None and (alpha.dtype != torch.float32 or tuple(alpha.shape) != (B, Hq)):
+        raise ValueError("alpha must be fp32 [B, Hq]")
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.sparse_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
+                                        _ptr(alpha), _ptr(out), B, Hq, Hkv, Lmax, d, _DTYPES[q.dtype],
+                                        _mode(mode), int(k_win), int(pi), int(M), int(seg), _stream(q.device))
+    if rc != SA_OK:
+        _raise(lib, rc, "sparse_attn_decode_noalloc")
     return out
 
 

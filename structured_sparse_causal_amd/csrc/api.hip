@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sparse_attn.h"
 #include "kernels.hpp"
 
@@ -349,14 +351,17 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d
 
 namespace {
 
-// Shared body of the three decode entry points.  Lplan: the largest position
+int scratch_for_current_device(void **out);
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+
+// Shared body of the decode entry points.  Lplan: the largest position
 // count the layout can hold (contiguous Lmax, ring R, paged max_pages * P);
 // cache_bytes: bytes of each cache tensor (overlap checks).
 int decode_impl(const void *q, const void *k_cache, const void *v_cache, const int *table, const int *cache_lens,
                 const float *alpha, void *o, int B, int Hq, int Hkv, int Lplan, int d, int dtype, int mode, int k_win,
                 int pi, int M, int seg, int layout, int R, int page_shift, int num_pages, int max_pages,
                 size_t cache_bytes, void *workspace, size_t workspace_bytes, void *stream,
-                const sa::FusedOpts &fo = sa::FusedOpts{}) {
+                const sa::FusedOpts &fo = sa::FusedOpts{}, bool noalloc = false) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || o == nullptr)
     return fail(SA_ERR_INVALID, "null tensor pointer");
   if (layout == sa::kCachePaged && table == nullptr) return fail(SA_ERR_INVALID, "null block table");
@@ -369,9 +374,15 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
     return fail(SA_ERR_INVALID, "misaligned tensor");
   if ((long long)Lplan * d >= (1LL << 31) || B > 65535) return fail(SA_ERR_INVALID, "problem too large");
   const size_t need = sparse_attn_decode_workspace_size(B, Hq, Hkv, Lplan, d, dtype, mode, k_win, pi, M, seg);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the decode workspace size");
-  if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes)
+      return fail(SA_ERR_WORKSPACE, "decode partial states exceed the 16 MiB device scratch of the allocation-free "
+                                    "decode (B * Hq * (window splits + 1) * (d + 4) * 4 bytes); use sparse_attn_decode");
+  } else {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the decode workspace size");
+    if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * Hq * d * es;
   const size_t ntab = layout == sa::kCachePaged ? (size_t)B * max_pages * 4 : 0;
@@ -393,6 +404,11 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
   da.table = table;
   da.opt = fo;
   if (fo.out_gate != nullptr && overlap(o, nq, fo.out_gate, nq)) return fail(SA_ERR_INVALID, "output overlaps out_gate");
+  if (noalloc) {   // every argument checked: now the library's device scratch
+    rc = scratch_for_current_device(&workspace);
+    if (rc != SA_OK) return rc;
+    da.ws = (float *)workspace;
+  }
   hipError_t e = sa::launch_decode(da, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   return SA_OK;
@@ -436,6 +452,58 @@ int sparse_attn_decode(const void *q, const void *k_cache, const void *v_cache, 
   const size_t nc = (size_t)B * Hkv * Lmax * d * elem_size(dtype);
   return decode_impl(q, k_cache, v_cache, nullptr, cache_lens, alpha, o, B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi,
                      M, seg, sa::kCacheContig, 0, 0, 0, 0, nc, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device scratch of the allocation-free decode: the split partial states live
+// in this file-scope array (one copy per GPU the library runs on, held until
+// the process ends).  Host code never passes the array's name to a kernel:
+// that name is a host-side stand-in, not a device address.  The address of
+// each device's copy is looked up once, with that device current, and kept.
+__device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch copy (SA_OK), or an error
+// code with the error text set.
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+    if (ptr == nullptr) return fail(SA_ERR_HIP, "scratch symbol has no device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_attn_decode_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+int sparse_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,
+                               const float *alpha, void *o, int B, int Hq, int Hkv, int Lmax, int d, int dtype,
+                               int mode, int k_win, int pi, int M, int seg, void *stream) {
+  g_err[0] = 0;
+  int rc = decode_head_checks(B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi, M, seg);
+  if (rc != SA_OK) return rc;
+  if ((long long)B * Hkv * Lmax >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
+  const size_t nc = (size_t)B * Hkv * Lmax * d * elem_size(dtype);
+  return decode_impl(q, k_cache, v_cache, nullptr, cache_lens, alpha, o, B, Hq, Hkv, Lmax, d, dtype, mode, k_win, pi,
+                     M, seg, sa::kCacheContig, 0, 0, 0, 0, nc, nullptr, 0, stream, sa::FusedOpts{}, true);
 }
 
 int sparse_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int *cache_lens,

@@ -359,3 +359,22 @@ def test_fwd_ex_checks_everything_before_the_first_launch(lib):
     assert fwd_ex(lib, opts(cosine=1), mode=PI, a=WS + 1024) == INVALID
     # an lse overlapping out_gate is rejected too
     assert fwd_ex(lib, opts(out_gate=OG), lse=OG + 64) == INVALID
+
+
+def test_decode_noalloc_checks(lib):
+    # the allocation-free decode: same argument checks as the decode, and
+    # partial states beyond its fixed device scratch are refused before any
+    # HIP call (the scratch address is looked up only after these checks)
+    limit = lib.sparse_attn_decode_noalloc_max_workspace()
+    assert limit == 16 << 20
+    args = (Q, K, V, A + 4096, A, O)
+    B = 1024
+    assert lib.sparse_attn_decode_workspace_size(B, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0) > limit
+    assert lib.sparse_attn_decode_noalloc(*args, B, 32, 8, 32768, 128, BF16, PI, 2048, 2048, 15, 0, None) == WORKSPACE
+    assert b"scratch" in lib.sparse_attn_last_error()
+    assert lib.sparse_attn_decode_noalloc(*args, 2, 8, 2, 512, 96, BF16, PI, 64, 64, 3, 0, None) == UNSUPPORTED
+    assert lib.sparse_attn_decode_noalloc(*args, 2, 8, 3, 512, 128, BF16, PI, 64, 64, 3, 0, None) == INVALID
+    assert lib.sparse_attn_decode_noalloc(Q, K, V, A + 4096, None, O, 2, 8, 2, 512, 128, BF16, PI, 64, 64, 3, 0,
+                                          None) == INVALID   # alpha required
+    assert lib.sparse_attn_decode_noalloc(Q, K, V, A + 4096, A, Q, 2, 8, 2, 512, 128, BF16, PI, 64, 64, 3, 0,
+                                          None) == INVALID   # o overlaps q
