@@ -73,13 +73,15 @@ def _load():
             f64 = ctypes.c_double
             lib.orc_fwd_rows_ex.restype = i32
             lib.orc_fwd_rows_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                            i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, i64, vp]
+                                            i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, vp, i64,
+                                            vp, i64, vp]
             lib.orc_decode_ex.restype = i32
             lib.orc_decode_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                          i32, i64, i64, i64, i64, f64, i32, vp, vp, vp]
+                                          i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, vp, i64, vp]
             lib.orc_lse_rows_ex.restype = i32
             lib.orc_lse_rows_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64,
-                                            i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, i64, vp]
+                                            i32, i64, i64, i64, i64, f64, i32, vp, vp, vp, vp, i64,
+                                            vp, i64, vp]
             lib.orc_bwd.restype = i32
             lib.orc_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                     i32, i64, i64, i64, i64, f64, vp, vp, vp, vp]
@@ -136,14 +138,35 @@ def key_set(i: int, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
     return keys[:n].copy(), labels[:n].copy()
 
 
-def _gate_args(gate_w, gate_b, Hq, d):
-    """Gate computed from the query: w [Hq, d], b [Hq] (fp32 inputs)."""
-    if gate_w is None:
-        return None, None
-    w32, b32 = _f32(gate_w), _f32(gate_b)
-    if w32.shape != (Hq, d) or b32.shape != (Hq,):
-        raise ValueError("oracle: gate_w must be [Hq, d] and gate_b [Hq]")
-    return w32, b32
+class _Gate:
+    """Gate network arguments as the C oracle takes them (fp32 arrays kept
+    alive for the call): one linear layer, w [Hq, d] and b [Hq]; or two
+    layers with a ReLU hidden layer of width H, w [Hq, H, d], b [Hq, H],
+    w2 [Hq, H], b2 [Hq]."""
+
+    def __init__(self, gate_w, gate_b, gate_w2, gate_b2, Hq, d):
+        self.arrays = [None, None, None, None]
+        self.hidden = 0
+        if gate_w is None:
+            if gate_b is not None or gate_w2 is not None or gate_b2 is not None:
+                raise ValueError("oracle: gate biases or second layer without gate_w")
+            return
+        w, b = _f32(gate_w), _f32(gate_b)
+        if gate_w2 is None:
+            if gate_b2 is not None or w.shape != (Hq, d) or b.shape != (Hq,):
+                raise ValueError("oracle: linear gate needs gate_w [Hq, d] and gate_b [Hq]")
+            self.arrays = [w, b, None, None]
+            return
+        w2, b2 = _f32(gate_w2), _f32(gate_b2)
+        H = w.shape[1] if w.ndim == 3 else -1
+        if H < 1 or w.shape != (Hq, H, d) or b.shape != (Hq, H) or w2.shape != (Hq, H) or b2.shape != (Hq,):
+            raise ValueError("oracle: gate MLP needs gate_w [Hq, H, d], gate_b [Hq, H], gate_w2 [Hq, H], "
+                             "gate_b2 [Hq]")
+        self.arrays = [w, b, w2, b2]
+        self.hidden = H
+
+    def args(self):
+        return [a.ctypes.data if a is not None else None for a in self.arrays] + [self.hidden]
 
 
 def _sigmoid(x):
@@ -160,15 +183,17 @@ def _out_gate(out, out_gate):
 
 def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
         seg: int = 0, rows=None, scale=None, cosine: bool = False, gate_w=None, gate_b=None,
-        out_gate=None) -> np.ndarray:
+        gate_w2=None, gate_b2=None, out_gate=None) -> np.ndarray:
     """Forward attention in fp64.
 
     q [B,Hq,N,d], k/v [B,Hkv,N,d], alpha [B,Hq,N] (PI only).  With ``rows``
     (flat ids (b*Hq+h)*N+i) returns [len(rows), d]; otherwise [B,Hq,N,d].
     Options: ``scale`` (default 1/sqrt(d)); ``cosine`` scores
-    scale * cos(q_i, k_j); ``gate_w`` [Hq,d] / ``gate_b`` [Hq]: alpha =
-    sigmoid(<w_h, q_i> + b_h) instead of the alpha input; ``out_gate``
-    (shaped like the output): o * sigmoid(out_gate).
+    scale * cos(q_i, k_j); the gate network instead of the alpha input:
+    ``gate_w`` [Hq,d] / ``gate_b`` [Hq] give alpha = sigmoid(<w_h, q_i> + b_h),
+    and with ``gate_w`` [Hq,H,d], ``gate_b`` [Hq,H], ``gate_w2`` [Hq,H],
+    ``gate_b2`` [Hq] alpha = sigmoid(sum_u w2_hu relu(<w_hu, q_i> + b_hu) + b2_h);
+    ``out_gate`` (shaped like the output): o * sigmoid(out_gate).
     """
     lib = _load()
     q32, k32, v32 = _f32(q), _f32(k), _f32(v)
@@ -187,14 +212,12 @@ def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
         out = np.empty((sel.size, d), dtype=np.float64)
         sel_p, nsel = sel.ctypes.data, sel.size
-    w32, b32 = _gate_args(gate_w, gate_b, Hq, d)
+    gate = _Gate(gate_w, gate_b, gate_w2, gate_b2, Hq, d)
     rc = lib.orc_fwd_rows_ex(q32.ctypes.data, k32.ctypes.data, v32.ctypes.data,
                              a32.ctypes.data if a32 is not None else None,
                              B, Hq, Hkv, N, d, m, int(k_win), int(pi), int(M), int(seg),
                              1.0 / np.sqrt(d) if scale is None else float(scale), int(bool(cosine)),
-                             w32.ctypes.data if w32 is not None else None,
-                             b32.ctypes.data if b32 is not None else None,
-                             sel_p, nsel, out.ctypes.data)
+                             *gate.args(), sel_p, nsel, out.ctypes.data)
     _check(rc)
     if out_gate is not None and rows is not None:
         out_gate = _f32(out_gate).reshape(-1, d)[np.asarray(rows, dtype=np.int64).ravel()]
@@ -202,7 +225,8 @@ def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0,
 
 
 def lse(q, k, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
-        rows=None, scale=None, cosine: bool = False, gate_w=None, gate_b=None) -> np.ndarray:
+        rows=None, scale=None, cosine: bool = False, gate_w=None, gate_b=None, gate_w2=None,
+        gate_b2=None) -> np.ndarray:
     """Log-sum-exp of each row's scores (natural log), fp64: [B,Hq,N], or
     [len(rows)] for flat row ids."""
     lib = _load()
@@ -219,14 +243,12 @@ def lse(q, k, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg:
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
         out = np.empty(sel.size, dtype=np.float64)
         sel_p, nsel = sel.ctypes.data, sel.size
-    w32, b32 = _gate_args(gate_w, gate_b, Hq, d)
+    gate = _Gate(gate_w, gate_b, gate_w2, gate_b2, Hq, d)
     rc = lib.orc_lse_rows_ex(q32.ctypes.data, k32.ctypes.data,
                              a32.ctypes.data if a32 is not None else None,
                              B, Hq, Hkv, N, d, _mode(mode), int(k_win), int(pi), int(M), int(seg),
                              1.0 / np.sqrt(d) if scale is None else float(scale), int(bool(cosine)),
-                             w32.ctypes.data if w32 is not None else None,
-                             b32.ctypes.data if b32 is not None else None,
-                             sel_p, nsel, out.ctypes.data)
+                             *gate.args(), sel_p, nsel, out.ctypes.data)
     _check(rc)
     return out
 
@@ -273,7 +295,7 @@ def bwd(q, k, v, alpha, dO, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, se
 
 def decode(q, k_cache, v_cache, lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
            M: int = 0, seg: int = 0, scale=None, cosine: bool = False, gate_w=None, gate_b=None,
-           out_gate=None) -> np.ndarray:
+           gate_w2=None, gate_b2=None, out_gate=None) -> np.ndarray:
     """Single-token decode in fp64: the query of sequence b is at position
     lens[b]-1 and attends that position's key set inside the cache.
     q [B,Hq,d], caches [B,Hkv,Lmax,d], lens [B], alpha [B,Hq] -> [B,Hq,d]."""
@@ -288,13 +310,12 @@ def decode(q, k_cache, v_cache, lens, alpha=None, *, mode, k_win: int = 0, pi: i
     ln = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
     a32 = _f32(alpha) if alpha is not None else None
     out = np.empty((B, Hq, d), dtype=np.float64)
-    w32, b32 = _gate_args(gate_w, gate_b, Hq, d)
+    gate = _Gate(gate_w, gate_b, gate_w2, gate_b2, Hq, d)
     rc = lib.orc_decode_ex(q32.ctypes.data, kc.ctypes.data, vc.ctypes.data, ln.ctypes.data,
                            a32.ctypes.data if a32 is not None else None,
                            B, Hq, Hkv, Lmax, d, _mode(mode), int(k_win), int(pi), int(M),
                            int(seg), 1.0 / np.sqrt(d) if scale is None else float(scale),
-                           int(bool(cosine)), w32.ctypes.data if w32 is not None else None,
-                           b32.ctypes.data if b32 is not None else None, out.ctypes.data)
+                           int(bool(cosine)), *gate.args(), out.ctypes.data)
     _check(rc)
     return _out_gate(out, out_gate)
 

@@ -45,8 +45,11 @@
  *     GSS-Transformer page, methodology item 1):
  *       score(i, j) = scale * <q_i, k_j> / (|q_i| |k_j|) + prior(i, j);
  *   - the gate computed from the query (pi-Attention section 2 item 3: a
- *     light per-token, per-head network produces alpha), read as one linear
- *     layer per head on the query: alpha_i = sigmoid(<w_h, q_i> + b_h).
+ *     light per-token, per-head network -- an MLP -- produces alpha), on the
+ *     query row as that network's input:
+ *       two layers (hidden width H > 0, ReLU hidden layer):
+ *         alpha_i = sigmoid( sum_u w2_hu * relu(<w1_hu, q_i> + b1_hu) + b2_h );
+ *       or one linear layer (H = 0): alpha_i = sigmoid(<w1_h, q_i> + b1_h).
  *   The output gate o * sigmoid(g) of the LT2 page (section 3) is elementwise
  *   on the output and applied by the Python wrapper.
  *   o_i        = sum_j exp(score(i,j) - max) v_j / sum_j exp(score(i,j) - max)
@@ -198,21 +201,67 @@ static int orc_check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int m
     return ORC_OK;
 }
 
+/* Gate network of one query head (see the header): w1 [H][d] (or [d] when
+   H = 0), b1 [H] (or one bias), w2 [H], b2 one bias.  NULL w1: no gate. */
+typedef struct {
+    const float *w1, *b1, *w2, *b2;
+    int64_t hidden;
+} orc_gate;
+
+static orc_gate orc_gate_of_head(const float *gate_w, const float *gate_b, const float *gate_w2,
+                                 const float *gate_b2, int64_t hidden, int64_t h, int64_t d)
+{
+    orc_gate g;
+    g.hidden = hidden;
+    if (gate_w == NULL) {
+        g.w1 = g.b1 = g.w2 = g.b2 = NULL;
+        return g;
+    }
+    if (hidden > 0) {
+        g.w1 = gate_w + h * hidden * d;
+        g.b1 = gate_b + h * hidden;
+        g.w2 = gate_w2 + h * hidden;
+        g.b2 = gate_b2 + h;
+    } else {
+        g.w1 = gate_w + h * d;
+        g.b1 = gate_b + h;
+        g.w2 = g.b2 = NULL;
+    }
+    return g;
+}
+
+/* Gate output z (before the sigmoid) for one query row. */
+static double orc_gate_logit(const orc_gate *g, const float *qrow, int64_t d)
+{
+    int64_t c, u;
+    if (g->hidden <= 0) {
+        double z = (double)*g->b1;
+        for (c = 0; c < d; ++c) z += (double)g->w1[c] * (double)qrow[c];
+        return z;
+    }
+    {
+        double z = (double)*g->b2;
+        for (u = 0; u < g->hidden; ++u) {
+            double a = (double)g->b1[u];
+            for (c = 0; c < d; ++c) a += (double)g->w1[u * d + c] * (double)qrow[c];
+            if (a > 0.0) z += (double)g->w2[u] * a; /* relu */
+        }
+        return z;
+    }
+}
+
 /* Priors of one row.  alpha must lie in (0, 1]; alpha = 1 makes the skip
    prior log(0) = -inf, which removes the skip keys from the softmax.  With a
-   gate (w_h: d weights, b_h: bias) alpha comes from the query row instead:
-   alpha = sigmoid(<w_h, q_i> + b_h). */
-static int orc_priors_q(int mode, const float *alpha, int64_t at, const float *qrow, const float *w_h,
-                        const float *b_h, int64_t d, double *lp, double *ls)
+   gate network alpha comes from the query row instead (see orc_gate_logit). */
+static int orc_priors_q(int mode, const float *alpha, int64_t at, const float *qrow, const orc_gate *gate,
+                        int64_t d, double *lp, double *ls)
 {
     double a;
-    int64_t c;
     *lp = 0.0;
     *ls = 0.0;
     if (mode != ORC_MODE_PI) return ORC_OK;
-    if (w_h != NULL) {
-        double z = (double)*b_h;
-        for (c = 0; c < d; ++c) z += (double)w_h[c] * (double)qrow[c];
+    if (gate != NULL && gate->w1 != NULL) {
+        const double z = orc_gate_logit(gate, qrow, d);
         a = 1.0 / (1.0 + exp(-z));
         *lp = log(a);
         *ls = log(1.0 - a);
@@ -228,7 +277,7 @@ static int orc_priors_q(int mode, const float *alpha, int64_t at, const float *q
 
 static int orc_priors(int mode, const float *alpha, int64_t at, double *lp, double *ls)
 {
-    return orc_priors_q(mode, alpha, at, NULL, NULL, NULL, 0, lp, ls);
+    return orc_priors_q(mode, alpha, at, NULL, NULL, 0, lp, ls);
 }
 
 /*
@@ -243,6 +292,7 @@ int orc_fwd_rows_ex(const float *q, const float *k, const float *v, const float 
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                     int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
                     double scale, int cosine, const float *gate_w, const float *gate_b,
+                    const float *gate_w2, const float *gate_b2, int64_t gate_hidden,
                     const int64_t *sel, int64_t nsel, double *out)
 {
     int64_t cap, total, r;
@@ -262,14 +312,15 @@ int orc_fwd_rows_ex(const float *q, const float *k, const float *v, const float 
         for (r = 0; r < nsel; ++r) {
             int64_t row = sel ? sel[r] : r, b, h, i, g, n;
             double lp, ls;
+            orc_gate gate;
             if (local_err != ORC_OK) continue;
             if (row < 0 || row >= total) { local_err = ORC_ERR_ARGS; continue; }
             i = row % N;
             h = (row / N) % Hq;
             b = row / (N * Hq);
             g = h / (Hq / Hkv);
-            if ((local_err = orc_priors_q(mode, alpha, row, q + row * d, gate_w ? gate_w + h * d : NULL,
-                                          gate_b ? gate_b + h : NULL, d, &lp, &ls)) != ORC_OK) continue;
+            gate = orc_gate_of_head(gate_w, gate_b, gate_w2, gate_b2, gate_hidden, h, d);
+            if ((local_err = orc_priors_q(mode, alpha, row, q + row * d, &gate, d, &lp, &ls)) != ORC_OK) continue;
             n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             orc_row(q + row * d, k + (b * Hkv + g) * N * d, v + (b * Hkv + g) * N * d,
@@ -292,7 +343,7 @@ int orc_fwd_rows(const float *q, const float *k, const float *v, const float *al
                  const int64_t *sel, int64_t nsel, double *out)
 {
     return orc_fwd_rows_ex(q, k, v, alpha, B, Hq, Hkv, N, d, mode, k_win, pi, M, seg,
-                           1.0 / sqrt((double)d), 0, NULL, NULL, sel, nsel, out);
+                           1.0 / sqrt((double)d), 0, NULL, NULL, NULL, NULL, 0, sel, nsel, out);
 }
 
 /*
@@ -306,7 +357,8 @@ int orc_fwd_rows(const float *q, const float *k, const float *v, const float *al
 int orc_decode_ex(const float *q, const float *kc, const float *vc, const int32_t *lens,
                   const float *alpha, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax,
                   int64_t d, int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
-                  double scale, int cosine, const float *gate_w, const float *gate_b, double *out)
+                  double scale, int cosine, const float *gate_w, const float *gate_b,
+                    const float *gate_w2, const float *gate_b2, int64_t gate_hidden, double *out)
 {
     int64_t cap, r;
     int err = orc_check_common(B, Hq, Hkv, d, mode, k_win, pi, M, seg);
@@ -327,9 +379,10 @@ int orc_decode_ex(const float *q, const float *kc, const float *vc, const int32_
         for (r = 0; r < B * Hq; ++r) {
             int64_t b = r / Hq, h = r % Hq, g = h / (Hq / Hkv), i = lens[b] - 1, n;
             double lp, ls;
+            orc_gate gate;
             if (local_err != ORC_OK) continue;
-            if ((local_err = orc_priors_q(mode, alpha, r, q + r * d, gate_w ? gate_w + h * d : NULL,
-                                          gate_b ? gate_b + h : NULL, d, &lp, &ls)) != ORC_OK) continue;
+            gate = orc_gate_of_head(gate_w, gate_b, gate_w2, gate_b2, gate_hidden, h, d);
+            if ((local_err = orc_priors_q(mode, alpha, r, q + r * d, &gate, d, &lp, &ls)) != ORC_OK) continue;
             n = orc_key_set(i, i + 1, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             orc_row(q + r * d, kc + (b * Hkv + g) * Lmax * d, vc + (b * Hkv + g) * Lmax * d,
@@ -352,7 +405,7 @@ int orc_decode(const float *q, const float *kc, const float *vc, const int32_t *
                double *out)
 {
     return orc_decode_ex(q, kc, vc, lens, alpha, B, Hq, Hkv, Lmax, d, mode, k_win, pi, M, seg,
-                         1.0 / sqrt((double)d), 0, NULL, NULL, out);
+                         1.0 / sqrt((double)d), 0, NULL, NULL, NULL, NULL, 0, out);
 }
 
 /*
@@ -365,6 +418,7 @@ int orc_lse_rows_ex(const float *q, const float *k, const float *alpha,
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                     int mode, int64_t k_win, int64_t pi, int64_t M, int64_t seg,
                     double scale, int cosine, const float *gate_w, const float *gate_b,
+                    const float *gate_w2, const float *gate_b2, int64_t gate_hidden,
                     const int64_t *sel, int64_t nsel, double *out)
 {
     int64_t cap, total, r;
@@ -383,6 +437,7 @@ int orc_lse_rows_ex(const float *q, const float *k, const float *alpha,
         for (r = 0; r < nsel; ++r) {
             int64_t row = sel ? sel[r] : r, b, h, i, g, n, t;
             double lp, ls, mx = -INFINITY, sum = 0.0;
+            orc_gate gate;
             const float *qrow, *kmat;
             if (local_err != ORC_OK) continue;
             if (row < 0 || row >= total) { local_err = ORC_ERR_ARGS; continue; }
@@ -390,8 +445,8 @@ int orc_lse_rows_ex(const float *q, const float *k, const float *alpha,
             h = (row / N) % Hq;
             b = row / (N * Hq);
             g = h / (Hq / Hkv);
-            if ((local_err = orc_priors_q(mode, alpha, row, q + row * d, gate_w ? gate_w + h * d : NULL,
-                                          gate_b ? gate_b + h : NULL, d, &lp, &ls)) != ORC_OK) continue;
+            gate = orc_gate_of_head(gate_w, gate_b, gate_w2, gate_b2, gate_hidden, h, d);
+            if ((local_err = orc_priors_q(mode, alpha, row, q + row * d, &gate, d, &lp, &ls)) != ORC_OK) continue;
             n = orc_key_set(i, N, mode, k_win, pi, M, seg, keys, labels, cap);
             if (n <= 0) { local_err = ORC_ERR_ARGS; continue; }
             qrow = q + row * d;
@@ -422,7 +477,7 @@ int orc_lse_rows(const float *q, const float *k, const float *alpha,
                  const int64_t *sel, int64_t nsel, double *out)
 {
     return orc_lse_rows_ex(q, k, alpha, B, Hq, Hkv, N, d, mode, k_win, pi, M, seg,
-                           1.0 / sqrt((double)d), 0, NULL, NULL, sel, nsel, out);
+                           1.0 / sqrt((double)d), 0, NULL, NULL, NULL, NULL, 0, sel, nsel, out);
 }
 
 /*

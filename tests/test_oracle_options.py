@@ -5,6 +5,8 @@
                attention branch of the hybrid GSS-Transformer page)
     gate_w/b   alpha = sigmoid(<w_h, q_i> + b_h) from the query (pi-Attention
                section 2 item 3: a light network per token and head)
+    gate MLP   alpha = sigmoid(sum_u w2_hu relu(<w1_hu, q_i> + b1_hu) + b2_h):
+               the same network with a ReLU hidden layer
     out_gate   y = o * sigmoid(g) (LT2 page, section 3: SDPA output gate)
 
 Pinned against torch's scaled_dot_product_attention (its ``scale`` argument,
@@ -109,3 +111,84 @@ def test_decode_options_equal_last_prefill_row():
     dec = oracle.decode(np.ascontiguousarray(q[:, :, -1]), k, v, lens,
                         out_gate=np.ascontiguousarray(g[:, :, -1]), **prm)
     assert np.abs(dec - full[:, :, -1]).max() < 1e-12
+
+
+def gate_mlp_alpha(q, w1, b1, w2, b2):
+    """alpha of the gate MLP in fp64 by torch: [B,Hq,N] from q [B,Hq,N,d],
+    w1 [Hq,H,d], b1 [Hq,H], w2 [Hq,H], b2 [Hq]."""
+    hid = torch.relu(torch.einsum("bhnd,hud->bhnu", t64(q), t64(w1)) + t64(b1)[None, :, None, :])
+    return torch.sigmoid((hid * t64(w2)[None, :, None, :]).sum(-1) + t64(b2)[None, :, None]).numpy()
+
+
+def test_gate_mlp_equals_explicit_alpha():
+    # alpha computed independently (torch, fp64) and passed on the pinned
+    # explicit-alpha path: the gate network enters only through alpha
+    B, H, N, d, Hg = 2, 3, 45, 16, 7
+    q, k, v = rnd((B, H, N, d), 31), rnd((B, H, N, d), 32), rnd((B, H, N, d), 33)
+    w1, b1 = rnd((H, Hg, d), 34, 0.4), rnd((H, Hg), 35, 0.5)
+    w2, b2 = rnd((H, Hg), 36, 0.4), rnd((H,), 37, 0.3)
+    prm = dict(mode="pi", k_win=4, pi=6, M=5)
+    alpha = gate_mlp_alpha(q, w1, b1, w2, b2)
+    assert 0.01 < alpha.min() and alpha.max() < 0.99 and alpha.std() > 0.1   # varied, not saturated
+    relu_off = (np.einsum("bhnd,hud->bhnu", q.astype(np.float64), w1) + b1[None, :, None, :]) <= 0
+    assert 0.2 < relu_off.mean() < 0.8                          # both sides of every ReLU are used
+    got = oracle.fwd(q, k, v, None, gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2, **prm)
+    ref = oracle.fwd(q, k, v, alpha.astype(np.float32), **prm)
+    assert np.abs(got - ref).max() < 1e-6                       # alpha passed as fp32 on the explicit path
+    lse = oracle.lse(q, k, None, gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2, **prm)
+    assert np.abs(lse - oracle.lse(q, k, alpha.astype(np.float32), **prm)).max() < 1e-6
+    lens = np.array([N, 17], dtype=np.int32)
+    qd = np.ascontiguousarray(np.stack([q[0, :, N - 1], q[1, :, 16]]))
+    dec = oracle.decode(qd, k, v, lens, gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2, **prm)
+    assert np.abs(dec[0] - got[0, :, N - 1]).max() < 1e-12
+    assert np.abs(dec[1] - oracle.fwd(q[:, :, :17].copy(), k[:, :, :17].copy(), v[:, :, :17].copy(), None,
+                                      gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2, **prm)[1, :, 16]).max() < 1e-12
+
+
+def test_gate_mlp_reduces_to_the_linear_gate():
+    # relu(z) - relu(-z) = z: hidden rows (w, -w), biases (b, -b) and output
+    # weights (1, -1) give the one-layer gate sigmoid(<w, q> + b) exactly
+    B, H, N, d = 1, 2, 30, 8
+    q, k, v = rnd((B, H, N, d), 41), rnd((B, H, N, d), 42), rnd((B, H, N, d), 43)
+    w, b = rnd((H, d), 44, 0.3), rnd((H,), 45)
+    w1 = np.ascontiguousarray(np.stack([w, -w], axis=1))
+    b1 = np.ascontiguousarray(np.stack([b, -b], axis=1))
+    w2 = np.tile(np.array([1.0, -1.0], np.float32), (H, 1))
+    b2 = np.zeros(H, np.float32)
+    prm = dict(mode="pi", k_win=3, pi=5, M=4)
+    lin = oracle.fwd(q, k, v, None, gate_w=w, gate_b=b, **prm)
+    mlp = oracle.fwd(q, k, v, None, gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2, **prm)
+    assert np.abs(lin - mlp).max() < 1e-14
+
+
+def test_gate_mlp_worked_example_e1():
+    # Q = K = 0: the network sees only its biases.  With hidden biases (1, 2),
+    # output weights (0.5, -0.3) and b2 = ln(1/3) + 0.1 the logit is ln(1/3),
+    # alpha = 1/4, and the output is worked example E1 (tests/golden).
+    import pathlib
+    fx = {}
+    for line in (pathlib.Path(__file__).parent / "golden" / "e1_pi_no_overlap.txt").read_text().splitlines():
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            fx[key] = vals
+    N, d, H = int(fx["N"][0]), 4, 1
+    q = np.zeros((1, H, N, d), np.float32)
+    v = np.repeat(np.arange(N, dtype=np.float32)[None, None, :, None], d, axis=3)
+    w1 = rnd((H, 2, d), 51)                                     # multiplies q = 0: any weights
+    b1 = np.array([[1.0, 2.0]], np.float32)
+    w2 = np.array([[0.5, -0.3]], np.float32)
+    b2 = np.array([math.log(1.0 / 3.0) + 0.1], np.float32)
+    o = oracle.fwd(q, q, v, None, mode="pi", k_win=int(fx["k_win"][0]), pi=int(fx["pi"][0]), M=int(fx["M"][0]),
+                   gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2)
+    expected = np.array([float(x) for x in fx["expected"]])
+    assert np.abs(o[0, 0, :, 0] - expected).max() < 1e-6      # b2 rounded to fp32: alpha = 1/4 to ~1e-8
+
+
+def test_gate_mlp_argument_checks():
+    q = rnd((1, 2, 8, 4), 61)
+    with pytest.raises(ValueError):
+        oracle.fwd(q, q, q, None, mode="pi", k_win=1, pi=3, M=2, gate_w=rnd((2, 3, 4), 62),
+                   gate_b=rnd((2, 3), 63), gate_w2=rnd((2, 2), 64), gate_b2=rnd((2,), 65))
+    with pytest.raises(ValueError):
+        oracle.fwd(q, q, q, None, mode="pi", k_win=1, pi=3, M=2, gate_w=rnd((2, 4), 62),
+                   gate_b=rnd((2,), 63), gate_b2=rnd((2,), 65))
