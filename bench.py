@@ -340,7 +340,8 @@ def run_decode_layouts(torch, sa, w, reps, warmup):
 def run_option_workloads(torch, sa, reps, warmup):
     """Fused gate and epilogue options at the benchmark shapes, each timed
     against the plain call on the same inputs (same useful FLOP or bytes):
-    cosine scores (ECP), the query-driven gate (pi-Attention), the output
+    cosine scores (ECP), the query-driven gate (pi-Attention: one layer, and
+    the two-layer network of hidden width 32), the output
     gate (ECP), and all three in the GQA decode."""
     from structured_sparse_causal_amd.inputs import WORKLOADS, decode_inputs, prefill_inputs
     dev = torch.device("cuda:0")
@@ -353,7 +354,7 @@ def run_option_workloads(torch, sa, reps, warmup):
     gen = torch.Generator(device="cpu")
     gen.manual_seed(99)
     for name, wname, opt in (("ecp_cosine", "ecp_bf16", "cosine"), ("pi_query_gate", "pi_bf16", "gate"),
-                             ("ecp_out_gate", "ecp_bf16", "out_gate")):
+                             ("pi_gate_network_h32", "pi_bf16", "network"), ("ecp_out_gate", "ecp_bf16", "out_gate")):
         w = WORKLOADS[wname]
         q, k, v, a = prefill_inputs(w, device=dev)
         prm = dict(mode=w.mode, k_win=w.k_win, pi=w.pi, M=w.M, seg=w.seg)
@@ -364,9 +365,14 @@ def run_option_workloads(torch, sa, reps, warmup):
         elif opt == "gate":
             kw = dict(gate_w=(0.5 * torch.randn((w.Hq, w.d), generator=gen) / math.sqrt(w.d)).to(dev),
                       gate_b=torch.randn((w.Hq,), generator=gen).to(dev))
+        elif opt == "network":   # two layers, ReLU hidden layer of width 32
+            kw = dict(gate_w=(torch.randn((w.Hq, 32, w.d), generator=gen) / math.sqrt(w.d)).to(dev),
+                      gate_b=(0.5 * torch.randn((w.Hq, 32), generator=gen)).to(dev),
+                      gate_w2=(1.5 * torch.randn((w.Hq, 32), generator=gen) / math.sqrt(32)).to(dev),
+                      gate_b2=(0.5 * torch.randn((w.Hq,), generator=gen)).to(dev))
         else:
             kw = dict(out_gate=torch.randn(q.shape, generator=gen).to(q.dtype).to(dev))
-        alpha = None if opt == "gate" else a
+        alpha = None if opt in ("gate", "network") else a
         ms_plain = timed(lambda: sa.fwd(q, k, v, a, out=out, **prm))
         ms_opt = timed(lambda: sa.fwd(q, k, v, alpha, out=out, **prm, **kw))
         flop, _ = prefill_useful(w)

@@ -261,12 +261,24 @@ int sparse_attn_decode_paged(const void *q, const void *k_pages, const void *v_p
  *                (the attention branch of the hybrid GSS-Transformer page,
  *                methodology item 1); q and k rows must be nonzero.  The
  *                forward keeps an L2-normalised copy of k in the workspace.
- *   gate_w, gate_b  PI mode: the gate is computed in-kernel from the query,
- *                alpha_i = sigmoid(<gate_w[h], q_i> + gate_b[h]) (pi-Attention
- *                section 2 item 3: a light per-token, per-head network; read
- *                here as one linear layer per head on the query), and the
- *                alpha argument is ignored.  gate_w fp32 [Hq, d], gate_b fp32
- *                [Hq], device memory (gate_w 16-byte, gate_b 4-byte aligned); both or neither.
+ *   gate_w, gate_b, gate_hidden, gate_w2, gate_b2
+ *                PI mode: the gate is computed in-kernel from the query by a
+ *                light per-token, per-head network (pi-Attention section 2
+ *                item 3: an MLP produces alpha), and the alpha argument is
+ *                ignored.  The query row is the network's input.
+ *                gate_hidden = H in [1, 32]: two layers with a ReLU hidden
+ *                layer of width H,
+ *                  alpha_i = sigmoid( sum_u gate_w2[h][u] *
+ *                            relu(<gate_w[h][u], q_i> + gate_b[h][u]) + gate_b2[h] ),
+ *                  gate_w fp32 [Hq, H, d], gate_b [Hq, H], gate_w2 [Hq, H],
+ *                  gate_b2 [Hq].  The first layer runs on the matrix cores
+ *                  with each fp32 weight split into two bf16 parts.
+ *                gate_hidden = 0: one linear layer,
+ *                  alpha_i = sigmoid(<gate_w[h], q_i> + gate_b[h]),
+ *                  gate_w fp32 [Hq, d], gate_b [Hq]; gate_w2, gate_b2 NULL.
+ *                Device memory; gate_w 16-byte aligned, the others 4-byte.
+ *                gate_w and gate_b go together; SA_ERR_INVALID for a missing
+ *                second layer, H outside [0, 32], or the gate outside PI mode.
  *   out_gate     output gate of the LT2 page (section 3): the result is
  *                o * sigmoid(out_gate), out_gate shaped and typed like o
  *                (decode: [B, Hq, d]), device memory, 16-byte aligned.
@@ -277,6 +289,9 @@ typedef struct sa_options {
   const float *gate_w;
   const float *gate_b;
   const void *out_gate;
+  int gate_hidden;
+  const float *gate_w2;
+  const float *gate_b2;
 } sa_options;
 
 /*

@@ -33,20 +33,52 @@ SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE = 0, -1,
 class SaOptions(ctypes.Structure):
     """struct sa_options of the C ABI (fused gate and epilogue options)."""
     _fields_ = [("score_scale", ctypes.c_float), ("cosine", ctypes.c_int),
-                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p), ("out_gate", ctypes.c_void_p)]
+                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p), ("out_gate", ctypes.c_void_p),
+                ("gate_hidden", ctypes.c_int), ("gate_w2", ctypes.c_void_p), ("gate_b2", ctypes.c_void_p)]
 
 
-def _options(score_scale=0.0, cosine=False, gate_w=None, gate_b=None, out_gate=None):
+def _gate_hidden(gate_w, gate_b, gate_w2, gate_b2, Hq, d) -> int:
+    """Check the gate network's tensors against Hq and d; returns its hidden
+    width H (0 for the one-layer gate).  One layer: gate_w [Hq, d], gate_b
+    [Hq].  Two layers (ReLU hidden layer): gate_w [Hq, H, d], gate_b [Hq, H],
+    gate_w2 [Hq, H], gate_b2 [Hq]."""
+    if gate_w is None:
+        if gate_b is not None or gate_w2 is not None or gate_b2 is not None:
+            raise ValueError("gate biases or second layer given without gate_w")
+        return 0
+    for t, name in ((gate_w, "gate_w"), (gate_b, "gate_b"), (gate_w2, "gate_w2"), (gate_b2, "gate_b2")):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous fp32 tensor" % name)
+    if gate_w2 is None and gate_b2 is None:
+        if tuple(gate_w.shape) != (Hq, d) or gate_b is None or tuple(gate_b.shape) != (Hq,):
+            raise ValueError("the one-layer gate needs gate_w [Hq, d] and gate_b [Hq]")
+        return 0
+    H = gate_w.shape[1] if gate_w.dim() == 3 else -1
+    if (H < 1 or tuple(gate_w.shape) != (Hq, H, d) or gate_b is None or tuple(gate_b.shape) != (Hq, H)
+            or gate_w2 is None or tuple(gate_w2.shape) != (Hq, H) or gate_b2 is None
+            or tuple(gate_b2.shape) != (Hq,)):
+        raise ValueError("the gate network needs gate_w [Hq, H, d], gate_b [Hq, H], gate_w2 [Hq, H], gate_b2 [Hq]")
+    if H > 32:
+        raise ValueError("the gate network's hidden width must be at most 32")
+    return H
+
+
+def _options(score_scale=0.0, cosine=False, gate_w=None, gate_b=None, out_gate=None, gate_w2=None,
+             gate_b2=None, gate_hidden=0):
     """SaOptions for the given keywords, or None when all are off."""
-    if not score_scale and not cosine and gate_w is None and gate_b is None and out_gate is None:
+    if (not score_scale and not cosine and gate_w is None and gate_b is None and out_gate is None
+            and gate_w2 is None and gate_b2 is None):
         return None
-    for t, name in ((gate_w, "gate_w"), (gate_b, "gate_b")):
+    for t, name in ((gate_w, "gate_w"), (gate_b, "gate_b"), (gate_w2, "gate_w2"), (gate_b2, "gate_b2")):
         if t is not None and t.dtype != torch.float32:
             raise ValueError("%s must be fp32" % name)
     return SaOptions(float(score_scale), int(bool(cosine)),
                      None if gate_w is None else gate_w.data_ptr(),
                      None if gate_b is None else gate_b.data_ptr(),
-                     None if out_gate is None else out_gate.data_ptr())
+                     None if out_gate is None else out_gate.data_ptr(),
+                     int(gate_hidden),
+                     None if gate_w2 is None else gate_w2.data_ptr(),
+                     None if gate_b2 is None else gate_b2.data_ptr())
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -189,17 +221,20 @@ def _workspace(nbytes: int, device, workspace):
 
 def fwd(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
         out=None, workspace=None, lse=None, score_scale: float = 0.0, cosine: bool = False,
-        gate_w=None, gate_b=None, out_gate=None):
+        gate_w=None, gate_b=None, out_gate=None, gate_w2=None, gate_b2=None):
     """Prefill forward: q [B,Hq,N,d], k/v [B,Hkv,N,d] (bf16 or fp32, on the
     GPU), alpha [B,Hq,N] fp32 for the gated mode.  Returns o [B,Hq,N,d].
     With ``lse`` (an fp32 [B,Hq,N] tensor) the row log-sum-exp is written
     too (the training forward).  Options (sa_options): score_scale, cosine,
-    gate_w [Hq,d] / gate_b [Hq] (alpha from the query), out_gate (like o)."""
+    the gate network on the query in place of alpha (gate_w [Hq,d] / gate_b
+    [Hq]: one layer; gate_w [Hq,H,d] / gate_b [Hq,H] / gate_w2 [Hq,H] /
+    gate_b2 [Hq]: two layers, ReLU hidden layer), out_gate (like o)."""
     lib = load_library()
-    _need_gpu(q, k, v, alpha, out, workspace, gate_w, gate_b, out_gate)
-    opt = _options(score_scale, cosine, gate_w, gate_b, out_gate)
+    _need_gpu(q, k, v, alpha, out, workspace, gate_w, gate_b, out_gate, gate_w2, gate_b2)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-d [B, H, N, d]")
+    hid = _gate_hidden(gate_w, gate_b, gate_w2, gate_b2, q.shape[1], q.shape[3])
+    opt = _options(score_scale, cosine, gate_w, gate_b, out_gate, gate_w2, gate_b2, hid)
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise NotImplementedError("q, k, v must share dtype bf16 or fp32")
     B, Hq, N, d = q.shape
@@ -302,15 +337,16 @@ def bwd(q, k, v, alpha, o, lse, dO, *, mode, k_win: int = 0, pi: int = 0, M: int
 
 def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
            M: int = 0, seg: int = 0, out=None, workspace=None, score_scale: float = 0.0,
-           cosine: bool = False, gate_w=None, gate_b=None, out_gate=None):
+           cosine: bool = False, gate_w=None, gate_b=None, out_gate=None, gate_w2=None, gate_b2=None):
     """Single-token decode: q [B,Hq,d], caches [B,Hkv,Lmax,d], cache_lens [B]
     int32 on the GPU, alpha [B,Hq] fp32 for the gated mode.  Returns o [B,Hq,d].
     Options as for ``fwd`` (bf16 only); out_gate is [B,Hq,d]."""
     lib = load_library()
-    _need_gpu(q, k_cache, v_cache, cache_lens, alpha, out, workspace, gate_w, gate_b, out_gate)
-    opt = _options(score_scale, cosine, gate_w, gate_b, out_gate)
+    _need_gpu(q, k_cache, v_cache, cache_lens, alpha, out, workspace, gate_w, gate_b, out_gate, gate_w2, gate_b2)
     if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, d] and caches [B, Hkv, Lmax, d]")
+    hid = _gate_hidden(gate_w, gate_b, gate_w2, gate_b2, q.shape[1], q.shape[2])
+    opt = _options(score_scale, cosine, gate_w, gate_b, out_gate, gate_w2, gate_b2, hid)
     if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise NotImplementedError("q and caches must share dtype bf16 or fp32")
     B, Hq, d = q.shape

@@ -149,6 +149,9 @@ sa::FusedOpts fused_opts(const sa_options *opt, int Hq) {
   f.gate_bh0 = 0;
   f.gate_hq = Hq;
   f.out_gate = opt != nullptr ? opt->out_gate : nullptr;
+  f.gate_hidden = opt != nullptr ? opt->gate_hidden : 0;
+  f.gate_w2 = opt != nullptr ? opt->gate_w2 : nullptr;
+  f.gate_b2 = opt != nullptr ? opt->gate_b2 : nullptr;
   return f;
 }
 
@@ -156,7 +159,13 @@ int check_opts(const sa::FusedOpts &f, int mode) {
   if (!(f.score_scale >= 0.f) || f.score_scale > 3.0e38f) return fail(SA_ERR_INVALID, "score_scale must be finite and >= 0");
   if ((f.gate_w == nullptr) != (f.gate_b == nullptr)) return fail(SA_ERR_INVALID, "gate_w and gate_b go together");
   if (f.gate_w != nullptr && mode != SA_MODE_PI) return fail(SA_ERR_INVALID, "the query-driven gate is a PI-mode option");
-  if (!aligned(f.gate_w, 16) || !aligned(f.gate_b, 4) || !aligned(f.out_gate, 16))
+  if (f.gate_hidden < 0 || f.gate_hidden > 32) return fail(SA_ERR_INVALID, "gate_hidden must lie in [0, 32]");
+  if (f.gate_hidden > 0 && (f.gate_w == nullptr || f.gate_w2 == nullptr || f.gate_b2 == nullptr))
+    return fail(SA_ERR_INVALID, "the gate network (gate_hidden > 0) needs gate_w, gate_b, gate_w2 and gate_b2");
+  if (f.gate_hidden == 0 && (f.gate_w2 != nullptr || f.gate_b2 != nullptr))
+    return fail(SA_ERR_INVALID, "gate_w2 / gate_b2 given without gate_hidden");
+  if (!aligned(f.gate_w, 16) || !aligned(f.gate_b, 4) || !aligned(f.gate_w2, 4) || !aligned(f.gate_b2, 4) ||
+      !aligned(f.out_gate, 16))
     return fail(SA_ERR_INVALID, "misaligned option tensor");
   return SA_OK;
 }
@@ -164,6 +173,11 @@ int check_opts(const sa::FusedOpts &f, int mode) {
 // Bytes of the L2-normalised key copy that cosine scores read.
 size_t khat_bytes(const sa::FusedOpts &f, int B, int Hkv, int N, int d, int dtype) {
   return f.cosine ? round_up((size_t)B * Hkv * N * d * elem_size(dtype), 256) : 0;
+}
+
+// Bytes of the alpha rows the two-layer gate network's pre-pass writes (PI).
+size_t gate_alpha_bytes(const sa::FusedOpts &f, int mode, int B, int Hq, int N) {
+  return (f.gate_hidden > 0 && mode == SA_MODE_PI) ? round_up((size_t)B * Hq * N * sizeof(float), 256) : 0;
 }
 
 int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, void *o, float *lse, int B, int Hq,
@@ -189,35 +203,53 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
         overlap(lse, nl, alpha, na) || overlap(lse, nl, fo.out_gate, ng))
       return fail(SA_ERR_INVALID, "lse overlaps a tensor");
   }
-  // Workspace: [L2-normalised key copy (cosine scores)] [skip-key partial state (pi with skip keys)].
+  // Workspace: [L2-normalised key copy (cosine scores)] [alpha from the gate
+  // network (PI, two-layer gate)] [skip-key partial state (pi with skip keys)].
   const size_t kh = khat_bytes(fo, B, Hkv, N, d, dtype);
+  const size_t ga = gate_alpha_bytes(fo, mode, B, Hq, N);
   const bool skips = has_skips(mode, k_win, pi, M, N);
   const int chunk = skips ? fwd_chunk_heads(B, Hq, Hkv, N, d, dtype) : 0;
   const FwdLayout L = skips ? fwd_layout(chunk, N, d, dtype) : FwdLayout{0, 0, 0};
-  const size_t need = kh + L.total;
+  const size_t need = kh + ga + L.total;
   if (need > 0) {
+    const size_t nh = fo.gate_hidden > 0 ? (size_t)fo.gate_hidden : 1;
+    const size_t ngw = fo.gate_w ? (size_t)Hq * nh * d * 4 : 0, ngb = fo.gate_b ? (size_t)Hq * nh * 4 : 0;
+    const size_t ngw2 = fo.gate_w2 ? (size_t)Hq * nh * 4 : 0, ngb2 = fo.gate_b2 ? (size_t)Hq * 4 : 0;
     if (workspace == nullptr || workspace_bytes < need)
       return fail(SA_ERR_WORKSPACE, "workspace missing or smaller than the forward workspace size");
     if (!aligned(workspace, 256)) return fail(SA_ERR_INVALID, "workspace must be 256-byte aligned");
     if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nkv) || overlap(workspace, need, v, nkv) ||
         overlap(workspace, need, o, nq) || overlap(workspace, need, alpha, na) ||
-        overlap(workspace, need, lse, lse != nullptr ? nl : 0) || overlap(workspace, need, fo.out_gate, ng))
+        overlap(workspace, need, lse, lse != nullptr ? nl : 0) || overlap(workspace, need, fo.out_gate, ng) ||
+        overlap(workspace, need, fo.gate_w, ngw) || overlap(workspace, need, fo.gate_b, ngb) ||
+        overlap(workspace, need, fo.gate_w2, ngw2) || overlap(workspace, need, fo.gate_b2, ngb2))
       return fail(SA_ERR_INVALID, "workspace overlaps a tensor");
   }
   hipStream_t s = (hipStream_t)stream;
+  sa::FusedOpts fk = fo;   // the options as the attention kernels take them
+  if (ga > 0) {
+    // alpha of every row from the gate network, once; the kernels then take it
+    // as their alpha input
+    float *wa = (float *)((char *)workspace + kh);
+    hipError_t e = sa::launch_gate_alpha(q, wa, B * Hq, Hq, N, d, dtype, fo, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
+    alpha = wa;
+    fk.gate_w = fk.gate_b = fk.gate_w2 = fk.gate_b2 = nullptr;
+    fk.gate_hidden = 0;
+  }
   if (kh > 0) {
     hipError_t e = sa::launch_normalize_rows(k, workspace, (long long)B * Hkv * N, d, dtype, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
     k = workspace;   // scores read the normalised keys
-    workspace = (char *)workspace + kh;
   }
+  workspace = (char *)workspace + kh + ga;
   sa::PrefillArgs pa;
   pa.q = q; pa.k = k; pa.v = v; pa.alpha = alpha; pa.o = o;
   pa.skip_ml = nullptr; pa.skip_acc = nullptr; pa.lse = lse;
   pa.B = B; pa.Hq = Hq; pa.Hkv = Hkv; pa.N = N; pa.d = d; pa.dtype = dtype;
   pa.mode = mode; pa.k_win = k_win; pa.seg = seg;
   pa.skip_first = N;
-  pa.opt = fo;
+  pa.opt = fk;
   if (!skips) {
     hipError_t e = sa::launch_prefill(pa, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
@@ -239,7 +271,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
     sk.acc = (char *)workspace + L.acc_off;
     sk.B = 1; sk.Hq = n; sk.Hkv = n / grp; sk.N = N; sk.d = d; sk.dtype = dtype;
     sk.pi = pi; sk.M = M; sk.m_min = (int)mm;
-    sk.opt = fo;
+    sk.opt = fk;
     sk.opt.gate_bh0 = bh0;
     sk.opt.out_gate = nullptr;
     hipError_t e = sa::launch_skip(sk, s);
@@ -253,7 +285,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *alpha, vo
     pc.skip_first = (int)(mm * pi);
     pc.lse = lse != nullptr ? lse + (size_t)bh0 * N : nullptr;
     pc.opt.gate_bh0 = bh0;
-    if (fo.out_gate != nullptr) pc.opt.out_gate = (const char *)fo.out_gate + (size_t)bh0 * head_elems * es;
+    if (fk.out_gate != nullptr) pc.opt.out_gate = (const char *)fk.out_gate + (size_t)bh0 * head_elems * es;
     e = sa::launch_prefill(pc, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, hipGetErrorString(e));
   }
@@ -288,7 +320,7 @@ size_t sparse_attn_fwd_ex_workspace_size(int B, int Hq, int Hkv, int N, int d, i
       check_mode(mode, k_win, pi, M, seg) != SA_OK)
     return 0;
   const sa::FusedOpts fo = fused_opts(opt, Hq);
-  return khat_bytes(fo, B, Hkv, N, d, dtype) +
+  return khat_bytes(fo, B, Hkv, N, d, dtype) + gate_alpha_bytes(fo, mode, B, Hq, N) +
          sparse_attn_fwd_workspace_size(B, Hq, Hkv, N, d, dtype, mode, k_win, pi, M, seg);
 }
 
@@ -681,6 +713,6 @@ const char *sparse_attn_status_string(int status) {
 
 const char *sparse_attn_last_error(void) { return g_err; }
 
-int sparse_attn_version(void) { return 100; }
+int sparse_attn_version(void) { return 101; }
 
 }  // extern "C"

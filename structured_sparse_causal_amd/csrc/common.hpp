@@ -162,4 +162,158 @@ __device__ __forceinline__ void dma4(const void *gbase, unsigned voff, unsigned 
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ---------------------------------------------------------------------------
+// Gate network on the query (pi-Attention section 2 item 3: a light per-token,
+// per-head network produces the gate alpha).  Two layers with a ReLU hidden
+// layer of width H <= 32:
+//   z = sum_u w2[u] * relu(<w1[u], q> + b1[u]) + b2,   alpha = sigmoid(z).
+// The hidden pre-activations are one more matrix product on the query
+// fragments a kernel already holds as the B operand of its score MFMAs (the
+// first-layer rows take the place of key rows).  The fp32 weights enter as
+// two bf16 parts, w1 = hi + lo, so the product keeps ~16 significant bits of
+// each weight; the query is bf16 already.
+// ---------------------------------------------------------------------------
+struct GateMlp {
+  const float *w1, *b1, *w2, *b2;   // [H][D], [H], [H], [1] of one head
+  int H;
+};
+
+// The network of head hg: first layer [H][D], biases [H], output weights [H], bias.
+__device__ __forceinline__ GateMlp make_gate(const float *w1, const float *b1, const float *w2, const float *b2, int H,
+                                             int hg, int D) {
+  GateMlp g;
+  g.H = H;
+  g.w1 = w1 + (size_t)hg * H * D;
+  g.b1 = b1 + (size_t)hg * H;
+  g.w2 = w2 + (size_t)hg * H;
+  g.b2 = b2 + hg;
+  return g;
+}
+
+// w = hi + lo with hi, lo bf16: hi by the hardware conversion, lo the
+// rounded residual (x - hi is exact in fp32), ~16 significant bits in all.
+__device__ __forceinline__ void split_bf16x8(const f32x4 &a, const f32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = e < 4 ? a[e] : b[e - 4];
+    hi[e] = (bf16)x;
+    lo[e] = (bf16)(x - (float)hi[e]);
+  }
+}
+
+// Sum over four hidden units u0..u0+3 of w2[u] relu(z[u] + b1[u]) (units >= H
+// contribute nothing); one 16-byte load each for b1 and w2 when all four exist
+// and both addresses are 16-byte aligned.
+__device__ __forceinline__ float gate_out4(const GateMlp &g, int u0, float z0, float z1, float z2, float z3, float s) {
+  if (u0 + 4 <= g.H && ((((uintptr_t)(g.b1 + u0)) | ((uintptr_t)(g.w2 + u0))) & 15) == 0) {
+    const f32x4 b = *(const f32x4 *)(g.b1 + u0), w = *(const f32x4 *)(g.w2 + u0);
+    s = fmaf(w[0], fmaxf(z0 + b[0], 0.f), s);
+    s = fmaf(w[1], fmaxf(z1 + b[1], 0.f), s);
+    s = fmaf(w[2], fmaxf(z2 + b[2], 0.f), s);
+    return fmaf(w[3], fmaxf(z3 + b[3], 0.f), s);
+  }
+  const float zz[4] = {z0, z1, z2, z3};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (u0 + e < g.H) s = fmaf(g.w2[u0 + e], fmaxf(zz[e] + g.b1[u0 + e], 0.f), s);
+  return s;
+}
+
+// Lanes in the v_mfma_f32_32x32x16_bf16 layout of the prefill: lane (c, h)
+// holds q[16 kk + 8 h .. +7] of query c in qf[kk].  The first layer's rows
+// are prepared once (hidden unit c of lane (c, h), bf16 hi/lo parts) and
+// reused for any number of 32-query blocks.
+template <int D>
+struct GateRows32 {
+  bf16x8 hi[D / 16], lo[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ GateRows32<D> gate_rows_32(const GateMlp &g, int lane) {
+  const int u = lane & 31, h = lane >> 5;
+  GateRows32<D> r;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    f32x4 a = f32x4{}, b = f32x4{};
+    if (u < g.H) {
+      const float *w = g.w1 + (size_t)u * D + 16 * kk + 8 * h;
+      a = *(const f32x4 *)w;
+      b = *(const f32x4 *)(w + 4);
+    }
+    split_bf16x8(a, b, r.hi[kk], r.lo[kk]);
+  }
+  return r;
+}
+
+// z for query c (the same in both lanes of the query).
+template <int D>
+__device__ __forceinline__ float gate_mlp_logit_32(const bf16x8 (&qf)[D / 16], const GateRows32<D> &r,
+                                                   const GateMlp &g, int lane) {
+  const int h = lane >> 5;
+  f32x16 z = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.hi[kk], qf[kk], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.lo[kk], qf[kk], z, 0, 0, 0);
+  }
+  // register j of lane (c, h): hidden unit 8 (j / 4) + 4 h + j % 4 of query c
+  float s = 0.f;
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4) s = gate_out4(g, 8 * a4 + 4 * h, z[4 * a4], z[4 * a4 + 1], z[4 * a4 + 2], z[4 * a4 + 3], s);
+  return half_swap_sum(s) + g.b2[0];
+}
+
+// fp32 prefill layout (v_mfma_f32_32x32x2f32): lane (c, h) holds q[2 kk + h].
+template <int D>
+__device__ __forceinline__ float gate_mlp_logit_32_f32(const float (&qf)[D / 2], const GateMlp &g, int lane) {
+  const int u = lane & 31, h = lane >> 5;
+  f32x16 z = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 2; ++kk) {
+    const float a = u < g.H ? g.w1[(size_t)u * D + 2 * kk + h] : 0.f;
+    z = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], z, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4) s = gate_out4(g, 8 * a4 + 4 * h, z[4 * a4], z[4 * a4 + 1], z[4 * a4 + 2], z[4 * a4 + 3], s);
+  return half_swap_sum(s) + g.b2[0];
+}
+
+// Lanes in the v_mfma_f32_16x16x32_bf16 layout of the skip pass and the
+// decode: lane (G, t) = (lane / 16, lane % 16) holds q[32 kk + 8 G .. +7] of
+// query column t in qf[kk].  Applies ONE head's network to every column and
+// returns z of column t (the same in its four lane groups): the product pairs
+// every first-layer row with every column, so a caller whose columns belong
+// to different heads calls it once per head and keeps that head's columns.
+template <int D>
+__device__ __forceinline__ float gate_mlp_logit_16(const bf16x8 (&qf)[D / 32], const GateMlp &g, int lane) {
+  const int G = lane >> 4, t = lane & 15;
+  float s = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    if (blk == 1 && g.H <= 16) break;
+    // A operand: hidden unit 16 blk + t (this lane's row), dims 32 kk + 8 G .. +7
+    f32x4 z = f32x4{};
+    const int u = 16 * blk + t;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      f32x4 a = f32x4{}, b = f32x4{};
+      if (u < g.H) {
+        const float *w = g.w1 + (size_t)u * D + 32 * kk + 8 * G;
+        a = *(const f32x4 *)w;
+        b = *(const f32x4 *)(w + 4);
+      }
+      bf16x8 hi, lo;
+      split_bf16x8(a, b, hi, lo);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qf[kk], z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qf[kk], z, 0, 0, 0);
+    }
+    // register j of lane (G, t): hidden unit 16 blk + 4 G + j of column t
+    s = gate_out4(g, 16 * blk + 4 * G, z[0], z[1], z[2], z[3], s);
+  }
+  s += wave_shfl_xor(s, 16);
+  s += wave_shfl_xor(s, 32);
+  return s + g.b2[0];
+}
+
 }  // namespace sa

@@ -544,24 +544,36 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(Params p) {
     ss += wave_shfl_xor(ss, 32);
     sl2 *= hvalid ? rsqrtf(ss) : 0.f;
   }
-  if (p.opt.gate_w != nullptr && p.mode == kModePi) {   // alpha = sigmoid(<w_h, q> + b_h)
-    const float *w = p.opt.gate_w + (size_t)(hvalid ? hq : 0) * D + 8 * G;
-    f32x4 wv[NQF][2];
-#pragma unroll
-    for (int kk = 0; kk < NQF; ++kk) {
-      wv[kk][0] = *(const f32x4 *)(w + 32 * kk);
-      wv[kk][1] = *(const f32x4 *)(w + 32 * kk + 4);
-    }
-    const float bh = p.opt.gate_b[hvalid ? hq : 0];
+  if (p.opt.gate_w != nullptr && p.mode == kModePi) {   // alpha = sigmoid(gate network of q)
     float z = 0.f;
+    if (p.opt.gate_hidden > 0) {
+      // Two layers, ReLU hidden layer.  The columns are different heads: one
+      // pass of the network per head of this workgroup, each keeping its column.
 #pragma unroll
-    for (int kk = 0; kk < NQF; ++kk)
+      for (int hd = 0; hd < NHD; ++hd) {
+        if (16 * hc + hd >= p.grp) break;
+        const GateMlp gm = make_gate(p.opt.gate_w, p.opt.gate_b, p.opt.gate_w2, p.opt.gate_b2, p.opt.gate_hidden,
+                                     g * p.grp + 16 * hc + hd, D);
+        const float zh = gate_mlp_logit_16<D>(qf, gm, lane);
+        if (t == hd) z = zh;
+      }
+    } else {
+      const float *w = p.opt.gate_w + (size_t)(hvalid ? hq : 0) * D + 8 * G;
+      f32x4 wv[NQF][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], wv[kk][e >> 2][e & 3], z);
-    z += wave_shfl_xor(z, 16);
-    z += wave_shfl_xor(z, 32);
+      for (int kk = 0; kk < NQF; ++kk) {
+        wv[kk][0] = *(const f32x4 *)(w + 32 * kk);
+        wv[kk][1] = *(const f32x4 *)(w + 32 * kk + 4);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z = fmaf((float)qf[kk][e], wv[kk][e >> 2][e & 3], z);
+      z += wave_shfl_xor(z, 16);
+      z += wave_shfl_xor(z, 32);
+      z += p.opt.gate_b[hvalid ? hq : 0];
+    }
     if (hvalid) {   // log2 alpha and log2(1 - alpha), overflow-free
-      z += bh;
       const float l1 = __log2f(1.0f + fast_exp2(-fabsf(z) * kLog2e));
       bias_loc = (z >= 0.f ? 0.f : z * kLog2e) - l1;
       bias_skip = (z <= 0.f ? 0.f : -z * kLog2e) - l1;

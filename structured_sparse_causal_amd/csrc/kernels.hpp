@@ -18,16 +18,24 @@ constexpr int kPrefillBN = 64;
 // Fused gate and epilogue options (all off when zero / null):
 //   score_scale > 0 replaces 1/sqrt(d); cosine: scores are scale * cos(q, k)
 //   (the key rows given to the kernels are already L2-normalised; the query's
-//   norm is taken in-kernel); gate_w [Hq][d] / gate_b [Hq]: alpha =
-//   sigmoid(<gate_w[h], q_i> + gate_b[h]) computed in-kernel (PI), where head
-//   h = (gate_bh0 + local (batch, head) index) % gate_hq; out_gate: output
-//   o * sigmoid(out_gate), same layout and dtype as o.
+//   norm is taken in-kernel); the gate network on the query (PI) for head
+//   h = (gate_bh0 + local (batch, head) index) % gate_hq (the prefill and the
+//   skip pass take the one-layer gate in-kernel and the two-layer network's
+//   alpha from a pre-pass; the decode evaluates both in-kernel):
+//   gate_hidden = 0: gate_w [Hq][d] / gate_b [Hq], alpha =
+//   sigmoid(<gate_w[h], q_i> + gate_b[h]); gate_hidden = H in [1, 32]:
+//   gate_w [Hq][H][d], gate_b [Hq][H], gate_w2 [Hq][H], gate_b2 [Hq], alpha =
+//   sigmoid(sum_u gate_w2[h][u] relu(<gate_w[h][u], q_i> + gate_b[h][u]) +
+//   gate_b2[h]); out_gate: output o * sigmoid(out_gate), same layout and dtype
+//   as o.
 struct FusedOpts {
   float score_scale;
   int cosine;
   const float *gate_w, *gate_b;
   int gate_bh0, gate_hq;
   const void *out_gate;
+  int gate_hidden;
+  const float *gate_w2, *gate_b2;
 };
 
 struct PrefillArgs {
@@ -85,6 +93,9 @@ struct BwdArgs {
   void *dgate;                      // dL/dg (bf16) when out_gate is given
   void *dO_gated;                   // workspace [B*Hq*N][d] bf16: dO * sigmoid(g)
 };
+// alpha [BH][N] of every query row from the two-layer gate network in o (head = bh % Hq).
+hipError_t launch_gate_alpha(const void *q, float *alpha, int BH, int Hq, int N, int d, int dtype, const FusedOpts &o,
+                             hipStream_t s);
 hipError_t launch_normalize_rows(const void *src, void *dst, long long rows, int d, int dtype, hipStream_t s);
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

@@ -684,6 +684,67 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
 
 }  // namespace
 
+// Gate network pre-pass: alpha of every query row from the two-layer gate
+// network (pi-Attention section 2 item 3), computed once and written to the
+// workspace, where the skip pass and the prefill take it as their alpha
+// input.  A wave takes kGateBlocks blocks of 32 rows of one (batch, head) in
+// the prefill's lane layout: the first layer's rows are loaded and split into
+// bf16 parts once, and each block is one matrix product on its query
+// fragments (gate_mlp_logit_32).  alpha is clamped to [FLT_MIN, 1]: a logit
+// below about -87 would otherwise give alpha = 0 (a -inf local prior).
+constexpr int kGateBlocks = 8;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gate_alpha_kernel(const T *q, float *alpha, int BH, int N, int Hq, int nwb,
+                                                         FusedOpts opt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, c = lane & 31;
+  const int gw = blockIdx.x * 4 + wave;           // global wave: (batch, head) and its range of row blocks
+  const int bh = gw / nwb, wb = gw % nwb;
+  if (bh >= BH) return;                           // the grid's last workgroup may hold spare waves (no barriers)
+  const GateMlp gm = make_gate(opt.gate_w, opt.gate_b, opt.gate_w2, opt.gate_b2, opt.gate_hidden, bh % Hq, D);
+  if constexpr (sizeof(T) == 2) {
+    const GateRows32<D> rows = gate_rows_32<D>(gm, lane);
+#pragma unroll 2
+    for (int blk = 0; blk < kGateBlocks; ++blk) {
+      const int qi = (wb * kGateBlocks + blk) * 32 + c;
+      if ((wb * kGateBlocks + blk) * 32 >= N) break;   // wave-uniform
+      const T *row = q + ((size_t)bh * N + (qi < N ? qi : N - 1)) * D;
+      bf16x8 qf[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8 *)(row + 16 * kk + 8 * h);
+      const float z = gate_mlp_logit_32<D>(qf, rows, gm, lane);
+      if (qi < N && h == 0) alpha[(size_t)bh * N + qi] = fmaxf(1.0f / (1.0f + __expf(-z)), 1.17549435e-38f);
+    }
+  } else {
+    for (int blk = 0; blk < kGateBlocks; ++blk) {
+      const int qi = (wb * kGateBlocks + blk) * 32 + c;
+      if ((wb * kGateBlocks + blk) * 32 >= N) break;   // wave-uniform
+      const T *row = q + ((size_t)bh * N + (qi < N ? qi : N - 1)) * D;
+      float qf[D / 2];
+#pragma unroll
+      for (int kk = 0; kk < D / 2; ++kk) qf[kk] = row[2 * kk + h];
+      const float z = gate_mlp_logit_32_f32<D>(qf, gm, lane);
+      if (qi < N && h == 0) alpha[(size_t)bh * N + qi] = fmaxf(1.0f / (1.0f + __expf(-z)), 1.17549435e-38f);
+    }
+  }
+}
+
+hipError_t launch_gate_alpha(const void *q, float *alpha, int BH, int Hq, int N, int d, int dtype, const FusedOpts &o,
+                             hipStream_t s) {
+  const int nwb = (N + 32 * kGateBlocks - 1) / (32 * kGateBlocks);   // waves per (batch, head)
+  const long long waves = (long long)BH * nwb;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (dtype == kBF16) {
+    if (d == 64) hipLaunchKernelGGL((gate_alpha_kernel<bf16, 64>), grid, dim3(256), 0, s, (const bf16 *)q, alpha, BH, N, Hq, nwb, o);
+    else hipLaunchKernelGGL((gate_alpha_kernel<bf16, 128>), grid, dim3(256), 0, s, (const bf16 *)q, alpha, BH, N, Hq, nwb, o);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((gate_alpha_kernel<float, 64>), grid, dim3(256), 0, s, (const float *)q, alpha, BH, N, Hq, nwb, o);
+    else hipLaunchKernelGGL((gate_alpha_kernel<float, 128>), grid, dim3(256), 0, s, (const float *)q, alpha, BH, N, Hq, nwb, o);
+  }
+  return hipGetLastError();
+}
+
 // L2-normalised copy of key rows (scaled cosine scores): 8 lanes per row,
 // 16-byte loads and stores.
 template <typename T, int D>

@@ -117,21 +117,51 @@ def test_fused_options_full_size_sampled():
     assert_close(o[rows], ref, "bf16", "pi query gate")
 
 
-def test_pi_query_gate_several_chunks_sampled():
+def gate_mlp_params(w, H, gen):
+    return ((torch.randn((w.Hq, H, w.d), generator=gen) / math.sqrt(w.d)).float(),
+            (0.5 * torch.randn((w.Hq, H), generator=gen)).float(),
+            (1.5 * torch.randn((w.Hq, H), generator=gen) / math.sqrt(H)).float(),
+            (0.5 * torch.randn((w.Hq,), generator=gen)).float())
+
+
+def test_pi_gate_network_full_size_sampled():
+    # the benchmark's gate-network leg: the pi workload with alpha from the
+    # two-layer gate (hidden width 32)
+    w = WORKLOADS["pi_bf16"]
+    say("full-size pi gate network")
+    gen = torch.Generator().manual_seed(97)
+    q, k, v, _ = prefill_inputs(w, device=DEV)
+    w1, b1, w2, b2 = gate_mlp_params(w, 32, gen)
+    o = sa.fwd(q, k, v, None, gate_w=w1.to(DEV), gate_b=b1.to(DEV), gate_w2=w2.to(DEV), gate_b2=b2.to(DEV),
+               **prm(w)).float().cpu().numpy().reshape(-1, w.d)
+    rows = sample_rows(np.random.default_rng(13), w.B, w.Hq, w.N, 4000)
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), None, rows=rows, gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2,
+                     **prm(w))
+    assert_close(o[rows], ref, "bf16", "pi gate network")
+
+
+@pytest.mark.parametrize("network", [False, True], ids=["linear", "network"])
+def test_pi_query_gate_several_chunks_sampled(network):
     # the query-driven gate with no alpha tensor, on a shape whose skip pass
     # and prefill run over several chunks of head groups
     w = WORKLOADS["pi_bf16"].replace(name="pi_gate_chunks", B=2, Hq=32, Hkv=8, N=32768, k_win=200, pi=700,
                                      M=20, seed=71)
-    say("pi query gate over chunks %s" % (w,))
+    say("pi query gate (%s) over chunks %s" % ("network" if network else "linear", w))
     whole = w.B * w.Hq * w.N * (8 + 2 * w.d)
     assert 0 < sa.fwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, torch.bfloat16, "pi", w.k_win, w.pi,
                                     w.M) < whole / 2
     gen = torch.Generator().manual_seed(98)
     q, k, v, _ = prefill_inputs(w, device=DEV)
-    gw, gb = gate_params(w, gen)
-    o = sa.fwd(q, k, v, None, gate_w=gw.to(DEV), gate_b=gb.to(DEV), **prm(w)).float().cpu().numpy().reshape(-1, w.d)
+    if network:
+        w1, b1, w2, b2 = gate_mlp_params(w, 20, gen)
+        gk = dict(gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2)
+    else:
+        gw, gb = gate_params(w, gen)
+        gk = dict(gate_w=gw, gate_b=gb)
+    o = sa.fwd(q, k, v, None, **{key: t.to(DEV) for key, t in gk.items()}, **prm(w)).float().cpu().numpy()
+    o = o.reshape(-1, w.d)
     rows = sample_rows(np.random.default_rng(12), w.B, w.Hq, w.N, 4000)
-    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), None, rows=rows, gate_w=gw, gate_b=gb, **prm(w))
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), None, rows=rows, **gk, **prm(w))
     assert_close(o[rows], ref, "bf16", "pi query gate, chunked")
 
 

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sparse_attn_version() == 100
+    assert lib.sparse_attn_version() == 101
     assert lib.sparse_attn_status_string(SA_OK) == b"ok"
     assert lib.sparse_attn_status_string(WORKSPACE) == b"workspace too small"
     assert lib.sparse_attn_status_string(12345) == b"unknown status"
@@ -287,8 +287,10 @@ def test_further_mask_modes_validation(lib):
         256 * ((2 * 8 * 3 * 132 * 4 + 255) // 256)
 
 
-def opts(score_scale=0.0, cosine=0, gate_w=None, gate_b=None, out_gate=None):
-    return ctypes.byref(binding.SaOptions(score_scale, cosine, gate_w, gate_b, out_gate))
+def opts(score_scale=0.0, cosine=0, gate_w=None, gate_b=None, out_gate=None, gate_hidden=0, gate_w2=None,
+         gate_b2=None):
+    return ctypes.byref(binding.SaOptions(score_scale, cosine, gate_w, gate_b, out_gate, gate_hidden, gate_w2,
+                                          gate_b2))
 
 
 def fwd_ex(lib, opt, q=Q, k=K, v=V, a=A, o=O, lse=None, B=1, Hq=2, Hkv=2, N=256, d=64, dtype=BF16, mode=WINDOW,
@@ -378,3 +380,32 @@ def test_decode_noalloc_checks(lib):
                                           None) == INVALID   # alpha required
     assert lib.sparse_attn_decode_noalloc(Q, K, V, A + 4096, A, Q, 2, 8, 2, 512, 128, BF16, PI, 64, 64, 3, 0,
                                           None) == INVALID   # o overlaps q
+
+
+GW2, GB2 = 0x40002000, 0x40003000
+
+
+@pytest.mark.parametrize("okw", [
+    dict(gate_w=GW, gate_b=GB, gate_hidden=33, gate_w2=GW2, gate_b2=GB2),    # hidden width beyond 32
+    dict(gate_w=GW, gate_b=GB, gate_hidden=-1),
+    dict(gate_w=GW, gate_b=GB, gate_hidden=8, gate_b2=GB2),                  # second layer missing
+    dict(gate_w=GW, gate_b=GB, gate_hidden=8, gate_w2=GW2),
+    dict(gate_w=GW, gate_b=GB, gate_w2=GW2, gate_b2=GB2),                    # second layer without a width
+    dict(gate_hidden=8, gate_w2=GW2, gate_b2=GB2),                           # no first layer
+    dict(gate_w=GW, gate_b=GB, gate_hidden=8, gate_w2=GW2 + 2, gate_b2=GB2), # misaligned
+])
+def test_gate_network_option_checks(lib, okw):
+    assert fwd_ex(lib, opts(**okw), mode=PI, a=None) == INVALID
+    assert lib.sparse_attn_decode_ex(Q, K, V, A + 4096, None, O, 2, 8, 2, 512, 128, BF16, PI, 64, 64, 3, 0,
+                                     opts(**okw), WS, 1 << 30, None) == INVALID
+
+
+def test_gate_network_accepted_without_alpha(lib):
+    # a complete two-layer gate needs no alpha: validation runs to the overlap check
+    assert fwd_ex(lib, opts(gate_w=GW, gate_b=GB, gate_hidden=8, gate_w2=GW2, gate_b2=GB2), mode=PI, a=None,
+                  o=Q) == INVALID
+    assert b"overlaps" in lib.sparse_attn_last_error()
+    # the backward takes no gate network
+    args = (Q, K, V, A, O, LSE, DO, DQ, DK, DV, DA, 1, 2, 2, 256, 64, BF16, PI, 32, 64, 3, 0)
+    assert lib.sparse_attn_bwd_ex(*args, opts(gate_w=GW, gate_b=GB, gate_hidden=8, gate_w2=GW2, gate_b2=GB2),
+                                  None, WS, 1 << 30, None) == UNSUPPORTED

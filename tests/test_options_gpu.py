@@ -1,6 +1,7 @@
 """Parity of the fused gate and epilogue options on the GPU with the fp64
-oracle: score scale, scaled cosine scores, the query-driven gate, and the
-output gate, in the forward (bf16, fp32), the decode and the backward."""
+oracle: score scale, scaled cosine scores, the query-driven gate (one linear
+layer, or the two-layer network with a ReLU hidden layer), and the output
+gate, in the forward (bf16, fp32), the decode and the backward."""
 from __future__ import annotations
 
 import numpy as np
@@ -31,6 +32,17 @@ def gate_params(w: Workload, seed):
     return gw, gb
 
 
+def gate_mlp_params(w: Workload, H, seed):
+    """Gate network weights: w1 [Hq,H,d], b1 [Hq,H], w2 [Hq,H], b2 [Hq] (fp32),
+    scaled so that alpha varies over (0, 1) and both sides of the ReLUs occur."""
+    g = torch.Generator().manual_seed(seed)
+    w1 = (torch.randn((w.Hq, H, w.d), generator=g) / np.sqrt(w.d)).float()
+    b1 = (0.5 * torch.randn((w.Hq, H), generator=g)).float()
+    w2 = (1.5 * torch.randn((w.Hq, H), generator=g) / np.sqrt(H)).float()
+    b2 = (0.5 * torch.randn((w.Hq,), generator=g)).float()
+    return w1, b1, w2, b2
+
+
 def out_gate(w: Workload, seed, shape=None):
     g = torch.Generator().manual_seed(seed)
     return torch.randn(shape or (w.B, w.Hq, w.N, w.d), generator=g).to(w.torch_dtype)
@@ -51,6 +63,14 @@ CASES = [
     (Workload("ogate_pi_f32", "pi", "f32", 1, 2, 2, 400, 64, k_win=30, pi=64, M=4, seed=139), dict(ogate=True)),
     (Workload("all_pi", "pi", "bf16", 1, 4, 2, 1100, 64, k_win=100, pi=90, M=10, seed=140),
      dict(score_scale=9.0, cosine=True, gate=True, ogate=True)),
+    # the gate network (two layers, ReLU hidden layer of width H)
+    (Workload("mlp_pi", "pi", "bf16", 2, 2, 2, 800, 64, k_win=100, pi=128, M=5, seed=161), dict(mlp=16)),
+    (Workload("mlp_pi_long_d128", "pi", "bf16", 1, 4, 2, 900, 128, k_win=30, pi=20, M=9, seed=162), dict(mlp=32)),
+    (Workload("mlp_pi_h20_gqa", "pi", "bf16", 1, 8, 2, 1500, 64, k_win=64, pi=96, M=12, seed=163), dict(mlp=20)),
+    (Workload("mlp_pi_f32", "pi", "f32", 1, 2, 1, 500, 64, k_win=40, pi=48, M=6, seed=164), dict(mlp=7)),
+    (Workload("mlp_pi_f32_d128", "pi", "f32", 1, 2, 2, 300, 128, k_win=20, pi=25, M=8, seed=165), dict(mlp=13)),
+    (Workload("mlp_all_pi_d128", "pi", "bf16", 1, 4, 4, 1000, 128, k_win=90, pi=100, M=7, seed=166),
+     dict(score_scale=9.0, cosine=True, mlp=24, ogate=True)),
 ]
 
 
@@ -64,6 +84,10 @@ def gpu_and_oracle_kwargs(w, o):
         gw, gb = gate_params(w, w.seed + 1)
         gk["gate_w"], gk["gate_b"] = gw.to(DEV), gb.to(DEV)
         ok["gate_w"], ok["gate_b"] = gw, gb
+    if o.get("mlp"):
+        w1, b1, w2, b2 = gate_mlp_params(w, o["mlp"], w.seed + 3)
+        gk.update(gate_w=w1.to(DEV), gate_b=b1.to(DEV), gate_w2=w2.to(DEV), gate_b2=b2.to(DEV))
+        ok.update(gate_w=w1, gate_b=b1, gate_w2=w2, gate_b2=b2)
     if o.get("ogate"):
         g = out_gate(w, w.seed + 2)
         gk["out_gate"], ok["out_gate"] = g.to(DEV), g
@@ -75,7 +99,7 @@ def test_forward_options(w, o):
     say("case %s %s" % (w.name, sorted(o)))
     q, k, v, a = prefill_inputs(w)
     gk, ok = gpu_and_oracle_kwargs(w, o)
-    alpha = a if w.mode == "pi" and not o.get("gate") else None
+    alpha = a if w.mode == "pi" and not o.get("gate") and not o.get("mlp") else None
     out = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), None if alpha is None else alpha.to(DEV), **prm(w), **gk)
     torch.cuda.synchronize()
     ref = oracle.fwd(q, k, v, alpha, **prm(w), **ok)
@@ -97,6 +121,14 @@ DEC_CASES = [
      dict(score_scale=11.0, cosine=True, gate=True, ogate=True)),
     (Workload("dec_opt_scale_window", "window", "bf16", 3, 8, 8, 1000, 64, k_win=300, decode=True, seed=142),
      dict(score_scale=0.05, ogate=True)),
+    # the gate network: 4, 16 and 24 query heads per KV head (one, four and
+    # two head chunks of a workgroup's columns)
+    (Workload("dec_mlp_gqa4", "pi", "bf16", 4, 16, 4, 3000, 128, k_win=200, pi=256, M=10, decode=True, seed=171),
+     dict(mlp=24)),
+    (Workload("dec_mlp_gqa16_d64", "pi", "bf16", 3, 32, 2, 2000, 64, k_win=150, pi=100, M=12, decode=True,
+              seed=172), dict(mlp=9)),
+    (Workload("dec_mlp_gqa24_all", "pi", "bf16", 2, 48, 2, 1500, 128, k_win=100, pi=128, M=9, decode=True,
+              seed=173), dict(score_scale=11.0, cosine=True, mlp=32, ogate=True)),
 ]
 
 
@@ -109,7 +141,7 @@ def test_decode_options(w, o):
     if o.get("ogate"):
         g = out_gate(w, w.seed + 2, shape=(w.B, w.Hq, w.d))
         gk["out_gate"], ok["out_gate"] = g.to(DEV), g
-    alpha = a if w.mode == "pi" and not o.get("gate") else None
+    alpha = a if w.mode == "pi" and not o.get("gate") and not o.get("mlp") else None
     out = sa.decode(q, kc, vc, lens, alpha, **prm(w), **gk)
     torch.cuda.synchronize()
     ref = oracle.decode(q.cpu(), kc.cpu(), vc.cpu(), lens.cpu(), None if alpha is None else alpha.cpu(),
