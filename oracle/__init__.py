@@ -63,8 +63,11 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            path = os.environ.get("SA_ORACLE_LIB")   # another build of this oracle (sanitizer runs)
+            if not path:
+                build(force=False)
+                path = _LIB
+            lib = ctypes.CDLL(path)
             i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
             lib.orc_key_set.restype = i64
             lib.orc_key_set.argtypes = [i64, i64, i32, i64, i64, i64, i64, vp, vp, i64]

@@ -102,7 +102,10 @@ class SparseAttnError(RuntimeError):
 
 
 def library_path() -> str:
-    return _LIB_PATH
+    """The library this binding loads: libsparse_attn.so beside this file, or
+    the build named by the SPARSE_ATTN_LIB environment variable (another
+    build of the same sources, e.g. one with host-side sanitizers)."""
+    return os.environ.get("SPARSE_ATTN_LIB") or _LIB_PATH
 
 
 def load_library():
@@ -111,10 +114,11 @@ def load_library():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB_PATH):
+        path = library_path()
+        if not os.path.exists(path):
             raise RuntimeError("libsparse_attn.so is not built (%s); run "
-                               "`python -c 'import __graft_entry__ as g; g.build()'`" % _LIB_PATH)
-        lib = ctypes.CDLL(_LIB_PATH)
+                               "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
+        lib = ctypes.CDLL(path)
         i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
         lib.sparse_attn_fwd_workspace_size.restype = sz
         lib.sparse_attn_fwd_workspace_size.argtypes = [i] * 11

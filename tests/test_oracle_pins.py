@@ -391,3 +391,26 @@ def test_gates_reject_zeros_and_wrong_masks():
     assert gate_failures(wrong, ref, "bf16") != []
     wref = oracle.fwd(q, k, v, mode="window", k_win=64)
     assert gate_failures(oracle.fwd(q, k, v, mode="window", k_win=63), wref, "bf16") != []
+
+
+def test_loop_closed_form_window_means():
+    """The looped block (LT2 page, section 1 and section 2.2) with Q = K = 0:
+    every application is a plain mean over the window, so with V[j, :] = j
+    the rows follow by hand.  Rows i <= k see [0, i] at every step:
+    O_1[i] = i/2, and inductively O_T[i] = i / 2^T.  Rows i >= T k see only
+    rows that are at least (T-1) k: O_1[i] = i - k/2, and inductively
+    O_T[i] = i - T k / 2.  All values are exact in bf16 here, so the rounded
+    feedback (V_{t+1} = bf16(O_t)) changes nothing."""
+    N, d, kw, T = 48, 4, 4, 4
+    q = np.zeros((1, 1, N, d), np.float32)
+    v = np.repeat(np.arange(N, dtype=np.float32)[None, None, :, None], d, axis=3)
+    outs = oracle.loop_fwd(q, q, v, steps=T, mode="window", k_win=kw)
+    assert len(outs) == T
+    i = np.arange(N, dtype=np.float64)
+    for t, o in enumerate(outs, start=1):
+        col = o[0, 0, :, 0]
+        assert np.array_equal(o, np.repeat(col[:, None], d, axis=1)[None, None])
+        assert np.array_equal(col[: kw + 1], i[: kw + 1] / 2.0 ** t)
+        assert np.array_equal(col[t * kw:], i[t * kw:] - t * kw / 2.0)
+    # a dropped feedback (V fixed) would give i - k/2 at every step
+    assert not np.array_equal(outs[-1][0, 0, T * kw:, 0], i[T * kw:] - kw / 2.0)
