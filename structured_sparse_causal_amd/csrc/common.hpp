@@ -54,6 +54,14 @@ __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
   return (unsigned short)(u >> 16);
 }
 
+// Four fp32 values rounded to bf16 (RNE, NaN stays NaN) by the hardware
+// conversion v_cvt_pk_bf16_f32, packed as four consecutive bf16.  Checked bit
+// for bit against f32_to_bf16_bits on gfx950 (ties, denormals, infinities).
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  const bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};
+  return make_uint2(__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi));
+}
+
 // Two transposed 4-element reads joined into one 8-element MFMA operand.  Whole
 // vectors are reinterpreted (no per-element extraction).
 __device__ __forceinline__ bf16x8 join_bf16x8(short4v lo, short4v hi) {

@@ -631,12 +631,7 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
         x[2] *= sigmoidf_fast(bf16_to_f32(gu.z));
         x[3] *= sigmoidf_fast(bf16_to_f32(gu.w));
       }
-      ushort4 u;
-      u.x = f32_to_bf16_bits(x[0]);
-      u.y = f32_to_bf16_bits(x[1]);
-      u.z = f32_to_bf16_bits(x[2]);
-      u.w = f32_to_bf16_bits(x[3]);
-      *(ushort4 *)(op + 32 * db + 8 * j4 + 4 * h) = u;
+      *(uint2 *)(op + 32 * db + 8 * j4 + 4 * h) = pack_bf16x4(x[0], x[1], x[2], x[3]);
     }
 }
 

@@ -207,14 +207,8 @@ __global__ __launch_bounds__(256) void skip_bf16_kernel(Params p) {
   // traffic; the relative rounding (2^-9) applies to the skip share only.
   bf16 *ap = (bf16 *)p.acc + row * D;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    ushort4 u;
-    u.x = f32_to_bf16_bits(acc[db][0]);
-    u.y = f32_to_bf16_bits(acc[db][1]);
-    u.z = f32_to_bf16_bits(acc[db][2]);
-    u.w = f32_to_bf16_bits(acc[db][3]);
-    *(ushort4 *)(ap + 16 * db + 4 * G) = u;
-  }
+  for (int db = 0; db < D / 16; ++db)
+    *(uint2 *)(ap + 16 * db + 4 * G) = pack_bf16x4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
 }
 
 // fp32 I/O: one thread per query row, plain loops.
