@@ -502,6 +502,16 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
             s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
           }
         }
+        // Issue order: four key-fragment reads ahead of the products, then one
+        // read per product (left alone, the compiler keeps two reads in
+        // flight and waits on LDS before every other product).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 4 LDS reads
+#pragma unroll
+        for (int i = 0; i < NKB * NQF - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // key j visible to query i iff lo(i) <= j <= hi(i); tile-local index
         // of register jj of block kb: 32kb + 8(jj/4) + 4h + jj%4
         if (hi_part && lo_part) {
@@ -598,6 +608,14 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(lo, hi), pb[kk], acc[db], 0, 0, 0);
         }
       }
+      // the same for the value fragments: four products' reads ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NKB * NDB - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     if (more) wait_dma();
