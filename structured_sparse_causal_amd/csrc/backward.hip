@@ -64,6 +64,10 @@ struct Params {
   // dO * sigmoid(g) to dO_gated, which the other kernels read as dO, and dg
   const bf16 *out_gate;
   bf16 *dgate, *dO_gated;
+  // no skip keys and no output gate: the dq kernel forms D_i and c_i itself
+  // (it holds the rows of dO already) and writes them for the dk/dv walk, in
+  // place of the prep pass
+  int fold_prep;
 };
 
 // ---- D_i = <dO_i, o_i>,  c_i = log2(alpha_i) - lse_i log2(e) -----------------
@@ -488,7 +492,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
     qf[kk] = qvalid ? *(const bf16x8 *)(p.q + row * D + 16 * kk + 8 * h) : bf16x8{};
     df[kk] = qvalid ? *(const bf16x8 *)(p.dO + row * D + 16 * kk + 8 * h) : bf16x8{};
   }
-  const float ci = qvalid ? p.cv[row] : 0.f, Di = qvalid ? p.Dv[row] : 0.f;
+  float ci, Di;
+  if (p.fold_prep) {
+    // D_i = <dO_i, o_i>: this lane's half of the row (the chunks it holds of
+    // dO), summed over the two wave halves; c_i as the prep pass forms it
+    float dsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk) {
+      const bf16x8 ov = qvalid ? *(const bf16x8 *)(p.o + row * D + 16 * kk + 8 * h) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)df[kk][e], (float)ov[e], dsum);
+    }
+    Di = half_swap_sum(dsum);
+    ci = 0.f;
+    if (qvalid) {
+      ci = -p.lse[row] * kLog2e;
+      if (p.mode == kModePi && p.alpha != nullptr) ci += __log2f(p.alpha[row]);
+      if (h == 0) {
+        p.Dv[row] = Di;
+        p.cv[row] = ci;
+      }
+    }
+  } else {
+    ci = qvalid ? p.cv[row] : 0.f;
+    Di = qvalid ? p.Dv[row] : 0.f;
+  }
   const int lo_i = key_lo(qi, p.mode, p.k_win, p.seg);
   f32x16 acc[NDB];
 #pragma unroll
@@ -752,7 +780,9 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
   p.dgate = (bf16 *)a.dgate;
   p.dO_gated = (bf16 *)a.dO_gated;
   const long long rows = (long long)a.B * a.Hq * a.N;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
+  p.fold_prep = p.out_gate == nullptr && p.dq_s == nullptr;
+  if (!p.fold_prep)
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
   if (p.out_gate != nullptr) p.dO = p.dO_gated;   // the rest differentiate the ungated attention
   p.P = (a.N + a.pi - 1) / (a.pi > 0 ? a.pi : 1);
   p.skip_first = 0;
