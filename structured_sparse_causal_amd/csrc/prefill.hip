@@ -351,17 +351,24 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
   }
   auto stage = [&](int j0, int buf) __attribute__((always_inline)) {
     const bf16 *kb = Kp + (size_t)j0 * D, *vb = Vp + (size_t)j0 * D;
-    const bool whole = j0 + TBN <= N;
+    // (two loops, so that the clamp's vector arithmetic is not formed and
+    // then discarded on every whole tile)
+    if (j0 + TBN <= N) {
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      unsigned off = soff[u];
-      if (!whole) {
-        const int row = (int)(off / RB);
-        off += (unsigned)((min(j0 + row, N - 1) - j0 - row) * RB);
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const unsigned kdst = lds0 + buf * TILE + 1024 * (PER_WAVE * wave_s + u);
+        dma16(kb, soff[u], kdst);
+        dma16(vb, soff[u], kdst + 2 * TILE);
       }
-      const unsigned kdst = lds0 + buf * TILE + 1024 * (PER_WAVE * wave_s + u);
-      dma16(kb, off, kdst);
-      dma16(vb, off, kdst + 2 * TILE);
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const int row = (int)(soff[u] / RB);
+        const unsigned off = soff[u] + (unsigned)((min(j0 + row, N - 1) - j0 - row) * RB);
+        const unsigned kdst = lds0 + buf * TILE + 1024 * (PER_WAVE * wave_s + u);
+        dma16(kb, off, kdst);
+        dma16(vb, off, kdst + 2 * TILE);
+      }
     }
   };
   // The first tile's loads go out before the query's, so the workgroup waits
