@@ -556,17 +556,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], dp[kb], 0, 0, 0);
         }
       }
-      const bool full = w_allvalid && (j0 + BN - 1 <= w_hi_first) && (j0 >= w_lo_last);
-      const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
+      // Masks only on tiles that some row of the wave sees in part (a
+      // wave-uniform branch): a hidden key's score becomes -inf, so its
+      // probability and dS are 0.
+      if (!(w_allvalid && (j0 + BN - 1 <= w_hi_first) && (j0 >= w_lo_last))) {
+        const int a0 = lo_i - j0 - 4 * h, span = hi_i - lo_i;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int o = 32 * kb + 8 * (jj >> 2) + (jj & 3);
+            if ((unsigned)(o - a0) > (unsigned)span) s[kb][jj] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int o = 32 * kb + 8 * (jj >> 2) + (jj & 3);
-          float pr = fast_exp2(fmaf(s[kb][jj], p.scale_log2, ci));
-          if (!full && (unsigned)(o - a0) > (unsigned)span) pr = 0.f;
-          s[kb][jj] = pr * (dp[kb][jj] - Di);
-        }
+        for (int jj = 0; jj < 16; ++jj)
+          s[kb][jj] = fast_exp2(fmaf(s[kb][jj], p.scale_log2, ci)) * (dp[kb][jj] - Di);
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -712,16 +719,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(Params p) {
           // element jj: query i0 + 32 qb2 + 8(jj/4) + 4h + jj%4, key kj
 #pragma unroll
           for (int j4 = 0; j4 < 4; ++j4) {
-            const int ql = 32 * qb2 + 8 * j4 + 4 * h;        // tile-local query of element 4 j4
-            const f32x4 cvv = *(const f32x4 *)(cq + ql);
-            const f32x4 dvv = *(const f32x4 *)(dq + ql);
+            const f32x4 cvv = *(const f32x4 *)(cq + 32 * qb2 + 8 * j4 + 4 * h);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int jj = 4 * j4 + e;
-              float pr = fast_exp2(fmaf(s[jj], p.scale_log2, cvv[e]));
-              if (!full && (unsigned)(i0 + ql + e - vis_lo) > vis_span) pr = 0.f;
-              s[jj] = pr;
-              if (want_dk) dp[jj] = pr * (dp[jj] - dvv[e]);
+            for (int e = 0; e < 4; ++e) s[4 * j4 + e] = fast_exp2(fmaf(s[4 * j4 + e], p.scale_log2, cvv[e]));
+          }
+          if (!full) {   // masks only where some query of the tile misses some key of the wave (wave-uniform branch)
+            const int a0 = i0 + 32 * qb2 + 4 * h - vis_lo;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+              if ((unsigned)(a0 + 8 * (jj >> 2) + (jj & 3)) > vis_span) s[jj] = 0.f;
+          }
+          if (want_dk) {
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+              const f32x4 dvv = *(const f32x4 *)(dq + 32 * qb2 + 8 * j4 + 4 * h);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dp[4 * j4 + e] = s[4 * j4 + e] * (dp[4 * j4 + e] - dvv[e]);
             }
           }
           // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
