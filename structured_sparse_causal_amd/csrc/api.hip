@@ -332,24 +332,18 @@ int sparse_attn_fwd_ex(const void *q, const void *k, const void *v, const float 
 }
 
 // Backward workspace: D_i and c_i per query row (+16 floats of padding for
-// the 16-byte vector loads at the tail), then, with skip keys, the skip-key
-// contributions in bf16: dq [rows][d], dk and dv [kv rows][d].
+// the 16-byte vector loads at the tail).  The skip-key contributions are
+// added into dq, dk and dv in place, after the window walks.
 struct BwdLayout {
-  size_t dv_off, cv_off, dqs_off, dks_off, dvs_off, total;
+  size_t dv_off, cv_off, total;
 };
 
-static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d, bool skips) {
+static BwdLayout bwd_layout(int B, int Hq, int N) {
   BwdLayout L;
-  const size_t rows = (size_t)B * Hq * N, kvrows = (size_t)B * Hkv * N;
+  const size_t rows = (size_t)B * Hq * N;
   size_t at = 0;
   L.dv_off = at; at += round_up((rows + 16) * sizeof(float), 256);
   L.cv_off = at; at += round_up((rows + 16) * sizeof(float), 256);
-  L.dqs_off = L.dks_off = L.dvs_off = 0;
-  if (skips) {
-    L.dqs_off = at; at += round_up(rows * d * 2, 256);
-    L.dks_off = at; at += round_up(kvrows * d * 2, 256);
-    L.dvs_off = at; at += round_up(kvrows * d * 2, 256);
-  }
   L.total = at;
   return L;
 }
@@ -618,7 +612,7 @@ size_t sparse_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int 
   if (dtype != SA_DTYPE_BF16 || check_shape(dtype, d) != SA_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 ||
       Hq % Hkv != 0 || check_mode(mode, k_win, pi, M, seg) != SA_OK)
     return 0;
-  return bwd_layout(B, Hq, Hkv, N, d, has_skips(mode, k_win, pi, M, N)).total;
+  return bwd_layout(B, Hq, N).total;
 }
 
 int sparse_attn_bwd(const void *q, const void *k, const void *v, const float *alpha, const void *o, const float *lse,
@@ -663,7 +657,7 @@ int sparse_attn_bwd_ex(const void *q, const void *k, const void *v, const float 
   const long long rows = (long long)B * Hq * N;
   if (rows >= (1LL << 31) || (long long)N * d >= (1LL << 31)) return fail(SA_ERR_INVALID, "problem too large");
   const bool skips = has_skips(mode, k_win, pi, M, N);
-  const BwdLayout L = bwd_layout(B, Hq, Hkv, N, d, skips);
+  const BwdLayout L = bwd_layout(B, Hq, N);
   const size_t nq = (size_t)rows * d * 2, nkv = (size_t)B * Hkv * N * d * 2, nr = (size_t)rows * 4;
   const size_t total = L.total + (out_gated ? round_up(nq, 256) : 0);
   if (workspace == nullptr || workspace_bytes < total)
@@ -685,9 +679,7 @@ int sparse_attn_bwd_ex(const void *q, const void *k, const void *v, const float 
   char *w = (char *)workspace;
   ba.Dv = (float *)(w + L.dv_off);
   ba.cv = (float *)(w + L.cv_off);
-  ba.dq_s = skips ? (void *)(w + L.dqs_off) : nullptr;
-  ba.dk_s = skips ? (void *)(w + L.dks_off) : nullptr;
-  ba.dv_s = skips ? (void *)(w + L.dvs_off) : nullptr;
+  ba.skips = skips ? 1 : 0;
   ba.B = B; ba.Hq = Hq; ba.Hkv = Hkv; ba.N = N; ba.d = d;
   ba.mode = mode; ba.k_win = k_win; ba.pi = pi; ba.M = M; ba.seg = seg;
   ba.m_min = skips ? (int)skip_m_min(k_win, pi) : 1;

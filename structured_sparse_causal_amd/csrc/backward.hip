@@ -21,21 +21,24 @@
 // alpha_i = 1.
 //
 // Kernels (one call runs them in this order):
-//   bwd_prep_kernel   D_i and c_i = log2(prior of local keys) - lse_i*log2(e)
-//   skip_bwd_kv_kernel / skip_bwd_q_kernel   (pi-Attention with skip keys)
-//       the skip-key contributions to dk, dv (key-owned) and dq, dalpha
-//       (query-owned), bf16, written to the workspace; 16x16 MFMA tiles over
-//       the residue chains i mod pi (one kernel when every chain is one tile)
+//   bwd_prep_kernel   (output gate only) dO * sigmoid(g), dg, D_i and c_i
 //   bwd_dq_kernel     query-stationary over the window / ECP keys: the
 //       forward's tile walk with S^T = K Q^T and dP^T = V dO^T on the matrix
 //       cores, dS, then dQ^T += K^T dS^T (K^T fragments by transposed LDS
-//       reads); adds the skip seed and writes dq (bf16) (and dalpha = 0 when
-//       no row has a skip key)
+//       reads); writes dq (bf16), dalpha = 0 on rows without skip keys, and
+//       (no output gate) D_i = <dO_i, o_i> and c_i = log2(prior of local
+//       keys) - lse_i*log2(e) from the rows it holds
 //   bwd_dkv_kernel    key-stationary: a workgroup keeps 128 keys (K and V as
 //       MFMA operands in registers) and walks the query tiles that attend
 //       them, for every query head of the GQA group: S = Q K^T, dP = dO V^T,
 //       dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposed LDS reads);
-//       adds the skip seed and writes dk, dv (bf16)
+//       writes dk, dv (bf16)
+//   skip_bwd_kv_kernel / skip_bwd_q_kernel   (pi-Attention with skip keys)
+//       the skip-key contributions to dk, dv (key-owned) and dq, dalpha
+//       (query-owned), added into the bf16 gradients the walks wrote; 16x16
+//       MFMA tiles over the residue chains i mod pi (one kernel when every
+//       chain is one tile).  Every row is added by exactly one wave, after
+//       the walks (same stream), so no two writers meet.
 // Q/dO and K/V tiles are staged with the direct-to-LDS loads and row swizzle
 // of the forward.
 #include "common.hpp"
@@ -53,7 +56,7 @@ struct Params {
   bf16 *dq, *dk, *dv;
   float *dalpha;
   float *Dv, *cv;                       // [B*Hq*N]
-  bf16 *dq_s, *dk_s, *dv_s;             // skip contributions, bf16 (nullptr without skips)
+  int skips;                            // pi-Attention with skip keys: the skip kernels run last
   int B, Hq, Hkv, N, mode, k_win, pi, M, m_min, seg, grp;
   int nqb, nkb;
   // skip-key residue chains: periods per residue, first position with a skip
@@ -64,9 +67,9 @@ struct Params {
   // dO * sigmoid(g) to dO_gated, which the other kernels read as dO, and dg
   const bf16 *out_gate;
   bf16 *dgate, *dO_gated;
-  // no skip keys and no output gate: the dq kernel forms D_i and c_i itself
-  // (it holds the rows of dO already) and writes them for the dk/dv walk, in
-  // place of the prep pass
+  // no output gate: the dq kernel forms D_i and c_i itself (it holds the
+  // rows of dO already) and writes them for the dk/dv walk and the skip
+  // kernels, in place of the prep pass
   int fold_prep;
 };
 
@@ -137,6 +140,17 @@ __device__ __forceinline__ bf16x4 lds_tr16(const bf16 *rows, int c0, int G, int 
   return as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src));
 }
 
+// Four fp32 values added to four bf16 values in memory (the sum rounded to
+// bf16 once).
+__device__ __forceinline__ void add_bf16x4(bf16 *dst, f32x4 x) {
+  ushort4 u = *(const ushort4 *)dst;
+  u.x = f32_to_bf16_bits(bf16_to_f32(u.x) + x[0]);
+  u.y = f32_to_bf16_bits(bf16_to_f32(u.y) + x[1]);
+  u.z = f32_to_bf16_bits(bf16_to_f32(u.z) + x[2]);
+  u.w = f32_to_bf16_bits(bf16_to_f32(u.w) + x[3]);
+  *(ushort4 *)dst = u;
+}
+
 // Four fp32 values rounded to bf16 and stored as 8 bytes.
 __device__ __forceinline__ void store_bf16x4(bf16 *dst, f32x4 x) {
   ushort4 u;
@@ -155,10 +169,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Key-stationary: one wave per (batch, KV head, residue, tile of 16 key
 // periods); loops over the GQA group's heads and the query-period tiles that
-// have these keys as skip keys; writes dk, dv skip partials (fp32, dk scaled).
+// have these keys as skip keys; adds the skip contributions to dk, dv.
 // WITH_Q (every residue chain is one tile: P - m_min <= 16): the single query
 // tile holds every query of the chain and every skip key of those queries is
-// in this key tile, so the wave also writes the dq skip partial and dalpha.
+// in this key tile, so the wave also adds the dq contribution and writes
+// dalpha.
 template <int D, bool WITH_Q>
 __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   constexpr int LD = D + 8, NK = D / 32, ND = D / 16;
@@ -273,9 +288,9 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
         for (int db = 0; db < ND; ++db)
           aq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(ks, 16 * db, G, t), dsb, f32x4{}, 0, 0, 0);
         if (qvalid) {
-          bf16 *dst = p.dq_s + qrow * D;
+          bf16 *dst = p.dq + qrow * D;
 #pragma unroll
-          for (int db = 0; db < ND; ++db) store_bf16x4(dst + 16 * db + 4 * G, aq[db] * p.scale);
+          for (int db = 0; db < ND; ++db) add_bf16x4(dst + 16 * db + 4 * G, aq[db] * p.scale);
           if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
         }
       }
@@ -285,14 +300,14 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   const size_t krow = (size_t)bg * N + ik;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
-    store_bf16x4(p.dk_s + krow * D + 16 * db + 4 * G, adk[db] * p.scale);
-    store_bf16x4(p.dv_s + krow * D + 16 * db + 4 * G, adv[db]);
+    add_bf16x4(p.dk + krow * D + 16 * db + 4 * G, adk[db] * p.scale);
+    add_bf16x4(p.dv + krow * D + 16 * db + 4 * G, adv[db]);
   }
 }
 
 // Query-stationary (residue chains longer than one tile): one wave per
 // (batch, head, residue, tile of 16 query periods); loops over the key-period
-// tiles of their skip keys; writes the dq skip partial (fp32, scaled) and dalpha.
+// tiles of their skip keys; adds the dq skip contribution and writes dalpha.
 template <int D>
 __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   constexpr int LD = D + 8, NK = D / 32, ND = D / 16;
@@ -365,15 +380,14 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   da += wave_shfl_xor(da, 32);
   if (!qvalid) return;
 #pragma unroll
-  for (int db = 0; db < ND; ++db) store_bf16x4(p.dq_s + qrow * D + 16 * db + 4 * G, aq[db] * p.scale);
+  for (int db = 0; db < ND; ++db) add_bf16x4(p.dq + qrow * D + 16 * db + 4 * G, aq[db] * p.scale);
   if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
 }
 
 // Store 16 accumulator values of a 32x32 C tile (rows 8(j/4) + 4h + j%4 of the
-// 32-row block db, column = this lane) as bf16, scaled, plus a bf16 seed.
+// 32-row block db, column = this lane) as bf16, scaled.
 template <int D>
-__device__ __forceinline__ void store_rows_bf16(bf16 *dst, const f32x16 (&acc)[D / 32], float scale,
-                                                const bf16 *seed, int h) {
+__device__ __forceinline__ void store_rows_bf16(bf16 *dst, const f32x16 (&acc)[D / 32], float scale, int h) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -382,13 +396,6 @@ __device__ __forceinline__ void store_rows_bf16(bf16 *dst, const f32x16 (&acc)[D
       float x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * scale;
-      if (seed != nullptr) {
-        const ushort4 sd = *(const ushort4 *)(seed + dim);
-        x[0] += bf16_to_f32(sd.x);
-        x[1] += bf16_to_f32(sd.y);
-        x[2] += bf16_to_f32(sd.z);
-        x[3] += bf16_to_f32(sd.w);
-      }
       ushort4 u;
       u.x = f32_to_bf16_bits(x[0]);
       u.y = f32_to_bf16_bits(x[1]);
@@ -593,10 +600,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(Params p) {
     __syncthreads();
   }
   if (!qvalid) return;
-  // rows below m_min * pi have no skip key: no seed, and a zero gate gradient
-  const bool seeded = p.dq_s != nullptr && qi >= p.skip_first;
-  store_rows_bf16<D>(p.dq + row * D, acc, p.scale, seeded ? p.dq_s + row * D : nullptr, h);
-  if (p.dalpha != nullptr && !seeded && h == 0) p.dalpha[row] = 0.f;
+  store_rows_bf16<D>(p.dq + row * D, acc, p.scale, h);
+  // rows below m_min * pi have no skip key: a zero gate gradient (the skip
+  // kernels write it on the other rows)
+  if (p.dalpha != nullptr && !(p.skips && qi >= p.skip_first) && h == 0) p.dalpha[row] = 0.f;
 }
 
 // Queries whose key range [key_lo(i), key_hi(i)] holds key j form the range
@@ -769,10 +776,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(Params p) {
     }
   }
   if (!kvalid) return;
-  // keys at or above N - m_min * pi are no query's skip key: no seed
-  const bool seeded = p.dk_s != nullptr && kj < N - p.skip_first;
-  if (want_dk) store_rows_bf16<D>(p.dk + krow * D, adk, p.scale, seeded ? p.dk_s + krow * D : nullptr, h);
-  if (want_dv) store_rows_bf16<D>(p.dv + krow * D, adv, 1.0f, seeded ? p.dv_s + krow * D : nullptr, h);
+  if (want_dk) store_rows_bf16<D>(p.dk + krow * D, adk, p.scale, h);
+  if (want_dv) store_rows_bf16<D>(p.dv + krow * D, adv, 1.0f, h);
 }
 
 template <int D>
@@ -782,7 +787,7 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
   p.dO = (const bf16 *)a.dO; p.alpha = a.alpha; p.lse = a.lse;
   p.dq = (bf16 *)a.dq; p.dk = (bf16 *)a.dk; p.dv = (bf16 *)a.dv; p.dalpha = a.dalpha;
   p.Dv = a.Dv; p.cv = a.cv;
-  p.dq_s = (bf16 *)a.dq_s; p.dk_s = (bf16 *)a.dk_s; p.dv_s = (bf16 *)a.dv_s;
+  p.skips = a.skips;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.mode = a.mode; p.k_win = a.k_win; p.pi = a.pi;
   p.M = a.M; p.m_min = a.m_min; p.seg = a.seg; p.grp = a.Hq / a.Hkv;
   p.nqb = (a.N + BM - 1) / BM;
@@ -793,37 +798,41 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
   p.dgate = (bf16 *)a.dgate;
   p.dO_gated = (bf16 *)a.dO_gated;
   const long long rows = (long long)a.B * a.Hq * a.N;
-  p.fold_prep = p.out_gate == nullptr && p.dq_s == nullptr;
-  if (!p.fold_prep)
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
-  if (p.out_gate != nullptr) p.dO = p.dO_gated;   // the rest differentiate the ungated attention
   p.P = (a.N + a.pi - 1) / (a.pi > 0 ? a.pi : 1);
   p.skip_first = 0;
   p.nqt = p.nkt = p.nwork_q = p.nwork_kv = 0;
-  if (p.dq_s != nullptr) {
+  if (p.skips) {
     // skips exist, so m_min * pi < N
     p.skip_first = a.m_min * a.pi;
     p.nqt = p.nkt = (p.P - a.m_min + 15) / 16;
     const long long wq = (long long)a.B * a.Hq * a.pi * p.nqt;
-    if (wq > (1LL << 30)) return hipErrorInvalidValue;   // wave count beyond the 1-D grid
+    if (wq > (1LL << 30)) return hipErrorInvalidValue;   // wave count beyond the 1-D grid (before any launch)
     p.nwork_q = (int)wq;
     p.nwork_kv = (int)((long long)a.B * a.Hkv * a.pi * p.nkt);
+  }
+  p.fold_prep = p.out_gate == nullptr;
+  if (!p.fold_prep)
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s, p, rows);
+  if (p.out_gate != nullptr) p.dO = p.dO_gated;   // the rest differentiate the ungated attention
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.Hq * p.nqb), dim3(256), 0, s, p);
+  // d = 64: one pass (two waves per SIMD; split passes measured 20 % slower
+  // there).  d = 128: the dV and dK passes (two waves each, against one for
+  // the joint kernel).
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 0>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 1>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
+  }
+  // The skip-key contributions last: they read D_i (formed above) and add
+  // into the gradients the walks have written.
+  if (p.skips) {
     if (p.nqt == 1) {
       hipLaunchKernelGGL((skip_bwd_kv_kernel<D, true>), dim3((p.nwork_kv + 3) / 4), dim3(256), 0, s, p);
     } else {
       hipLaunchKernelGGL((skip_bwd_kv_kernel<D, false>), dim3((p.nwork_kv + 3) / 4), dim3(256), 0, s, p);
       hipLaunchKernelGGL((skip_bwd_q_kernel<D>), dim3((p.nwork_q + 3) / 4), dim3(256), 0, s, p);
     }
-  }
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.Hq * p.nqb), dim3(256), 0, s, p);
-  // d = 64: one pass (252 VGPRs, two waves per SIMD; split passes measured
-  // 20 % slower there).  d = 128: the dV and dK passes (two waves each,
-  // against one for the joint kernel).
-  if constexpr (D == 64) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 0>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
-  } else {
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 1>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2>), dim3(a.B * a.Hkv * p.nkb), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -85,7 +85,7 @@ struct BwdArgs {
   void *dq, *dk, *dv;               // bf16
   float *dalpha;                    // [B,Hq,N] or nullptr
   float *Dv, *cv;                   // workspace [B*Hq*N (+pad)]
-  void *dq_s, *dk_s, *dv_s;  // workspace skip contributions (bf16), or nullptr
+  int skips;                        // pi-Attention with skip keys (skip kernels after the walks)
   int B, Hq, Hkv, N, d;
   int mode, k_win, pi, M, m_min, seg;
   float score_scale;                // 0: 1/sqrt(d)

@@ -190,13 +190,12 @@ def test_bwd_workspace_sizes(lib):
     ws = lib.sparse_attn_bwd_workspace_size
     r256 = lambda x: -(-x // 256) * 256
     # Per query row D_i = dO_i . o_i and c_i (lse and log-gate term), each with a
-    # 16-float tail; with skip keys also bf16 skip partials of dq, dk, dv.
-    rows, kv = 2 * 16 * 4096, 2 * 16 * 4096
+    # 16-float tail; the skip-key contributions are added into dq, dk and dv in
+    # place, so skip keys need no more.
+    rows = 2 * 16 * 4096
     assert ws(2, 16, 16, 4096, 64, BF16, WINDOW, 256, 0, 0, 0) == 2 * r256((rows + 16) * 4)
-    assert ws(2, 16, 16, 4096, 64, BF16, PI, 256, 1024, 3, 0) == (
-        2 * r256((rows + 16) * 4) + r256(rows * 64 * 2) + 2 * r256(kv * 64 * 2))
-    assert ws(1, 8, 2, 1000, 128, BF16, PI, 60, 70, 8, 0) == (
-        2 * r256((8000 + 16) * 4) + r256(8000 * 128 * 2) + 2 * r256(2000 * 128 * 2))
+    assert ws(2, 16, 16, 4096, 64, BF16, PI, 256, 1024, 3, 0) == 2 * r256((rows + 16) * 4)
+    assert ws(1, 8, 2, 1000, 128, BF16, PI, 60, 70, 8, 0) == 2 * r256((8000 + 16) * 4)
     assert ws(1, 2, 2, 256, 64, BF16, PI, 300, 64, 4, 0) == 2 * r256((512 + 16) * 4)   # skips inside window
     assert ws(1, 2, 2, 256, 64, BF16, ECP, 0, 0, 0, 64) == 2 * r256((512 + 16) * 4)
     assert ws(1, 2, 2, 256, 64, F32, WINDOW, 8, 0, 0, 0) == 0                        # bf16 only
