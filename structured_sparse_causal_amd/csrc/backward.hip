@@ -151,6 +151,15 @@ __device__ __forceinline__ void add_bf16x4(bf16 *dst, f32x4 x) {
   *(ushort4 *)dst = u;
 }
 
+// Four fp32 values added to four bf16 values read earlier (old) and stored.
+__device__ __forceinline__ void add_old_bf16x4(bf16 *dst, ushort4 u, f32x4 x) {
+  u.x = f32_to_bf16_bits(bf16_to_f32(u.x) + x[0]);
+  u.y = f32_to_bf16_bits(bf16_to_f32(u.y) + x[1]);
+  u.z = f32_to_bf16_bits(bf16_to_f32(u.z) + x[2]);
+  u.w = f32_to_bf16_bits(bf16_to_f32(u.w) + x[3]);
+  *(ushort4 *)dst = u;
+}
+
 // Four fp32 values rounded to bf16 and stored as 8 bytes.
 __device__ __forceinline__ void store_bf16x4(bf16 *dst, f32x4 x) {
   ushort4 u;
@@ -201,6 +210,14 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   for (int kk = 0; kk < NK; ++kk) {
     kf[kk] = *(const bf16x8 *)(Kp + (size_t)ik * D + 32 * kk + 8 * G);
     vf[kk] = *(const bf16x8 *)(Vp + (size_t)ik * D + 32 * kk + 8 * G);
+  }
+  // the dk, dv rows the walks wrote, read now so the add at the end waits on nothing
+  const size_t krow = (size_t)bg * N + ik;
+  ushort4 dk0[ND], dv0[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    dk0[db] = *(const ushort4 *)(p.dk + krow * D + 16 * db + 4 * G);
+    dv0[db] = *(const ushort4 *)(p.dv + krow * D + 16 * db + 4 * G);
   }
   if (WITH_Q) {
 #pragma unroll
@@ -297,11 +314,10 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
     }
   }
   if (!kvalid) return;
-  const size_t krow = (size_t)bg * N + ik;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
-    add_bf16x4(p.dk + krow * D + 16 * db + 4 * G, adk[db] * p.scale);
-    add_bf16x4(p.dv + krow * D + 16 * db + 4 * G, adv[db]);
+    add_old_bf16x4(p.dk + krow * D + 16 * db + 4 * G, dk0[db], adk[db] * p.scale);
+    add_old_bf16x4(p.dv + krow * D + 16 * db + 4 * G, dv0[db], adv[db]);
   }
 }
 
