@@ -140,18 +140,8 @@ __device__ __forceinline__ bf16x4 lds_tr16(const bf16 *rows, int c0, int G, int 
   return as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src));
 }
 
-// Four fp32 values added to four bf16 values in memory (the sum rounded to
-// bf16 once).
-__device__ __forceinline__ void add_bf16x4(bf16 *dst, f32x4 x) {
-  ushort4 u = *(const ushort4 *)dst;
-  u.x = f32_to_bf16_bits(bf16_to_f32(u.x) + x[0]);
-  u.y = f32_to_bf16_bits(bf16_to_f32(u.y) + x[1]);
-  u.z = f32_to_bf16_bits(bf16_to_f32(u.z) + x[2]);
-  u.w = f32_to_bf16_bits(bf16_to_f32(u.w) + x[3]);
-  *(ushort4 *)dst = u;
-}
-
-// Four fp32 values added to four bf16 values read earlier (old) and stored.
+// Four fp32 values x added to four bf16 values u (read from dst earlier) and
+// stored to dst: the sum rounded to bf16 once.
 __device__ __forceinline__ void add_old_bf16x4(bf16 *dst, ushort4 u, f32x4 x) {
   u.x = f32_to_bf16_bits(bf16_to_f32(u.x) + x[0]);
   u.y = f32_to_bf16_bits(bf16_to_f32(u.y) + x[1]);
@@ -160,15 +150,8 @@ __device__ __forceinline__ void add_old_bf16x4(bf16 *dst, ushort4 u, f32x4 x) {
   *(ushort4 *)dst = u;
 }
 
-// Four fp32 values rounded to bf16 and stored as 8 bytes.
-__device__ __forceinline__ void store_bf16x4(bf16 *dst, f32x4 x) {
-  ushort4 u;
-  u.x = f32_to_bf16_bits(x[0]);
-  u.y = f32_to_bf16_bits(x[1]);
-  u.z = f32_to_bf16_bits(x[2]);
-  u.w = f32_to_bf16_bits(x[3]);
-  *(ushort4 *)dst = u;
-}
+// The same with the bf16 values read from dst now.
+__device__ __forceinline__ void add_bf16x4(bf16 *dst, f32x4 x) { add_old_bf16x4(dst, *(const ushort4 *)dst, x); }
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
