@@ -473,7 +473,7 @@ def main():
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (one MI355X per box); "
+        print("bench.py: the library runs on one GPU (no sharding or collectives); "
               "--gpus %d is not supported. Run with --gpus 1." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
