@@ -1,12 +1,12 @@
 """Prefill parity on seeded random shapes and mask parameters.
 
-Twenty-four configurations drawn once from a fixed seed: every mask mode,
+Ninety-six configurations drawn once from a fixed seed: every mask mode,
 d = 64 and 128, bf16 and fp32, GQA ratios 1-4, sequence lengths that are not
 multiples of the 128-row query blocks or the key tiles, windows and segments
 of any size (including wider than the sequence) and skip periods below and
 above the window.  Every output element is compared with the fp64 oracle.
-Twelve more (bf16) run the training forward and the backward and compare
-every gradient element with the oracle's fp64 chain rule, and twelve
+Forty-eight more (bf16) run the training forward and the backward and compare
+every gradient element with the oracle's fp64 chain rule, and forty-eight
 decode cases with ragged cache lengths compare every output element.
 """
 from __future__ import annotations
@@ -25,7 +25,7 @@ DEV = torch.device("cuda:0")
 MODES = ["pi", "window", "ecp", "window_bidir", "ssplit", "ecp_full"]
 
 
-def _cases(n=24, seed=2024):
+def _cases(n=96, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for idx in range(n):
@@ -57,7 +57,7 @@ def test_random_shape(w):
     assert_close(o.float().cpu().numpy(), ref, w.dtype, w.name)
 
 
-def _bwd_cases(n=12, seed=4048):
+def _bwd_cases(n=48, seed=4048):
     rng = np.random.default_rng(seed)
     out = []
     for idx in range(n):
@@ -98,7 +98,7 @@ def test_random_shape_backward(w):
         assert_grad_close(da.cpu().numpy(), ra, w.name + " dalpha")
 
 
-def _decode_cases(n=12, seed=8096):
+def _decode_cases(n=48, seed=8096):
     rng = np.random.default_rng(seed)
     out = []
     for idx in range(n):
