@@ -352,7 +352,7 @@ static BwdLayout bwd_layout(int B, int Hq, int N) {
 // 2*seg - 1 for ECP, never more than Lmax - 1) are cut into splits of about 256
 // rows (a multiple of 64, the rows one pass of a 4-wave workgroup covers); one
 // more split holds the query row and the skip keys.
-static void decode_plan(int Lmax, int mode, int k_win, int pi, int M, int seg, int *n_wsplit, int *chunk,
+static void decode_plan(int Lmax, int mode, int k_win, int pi, int seg, int *n_wsplit, int *chunk,
                         int *m_min) {
   long long range = mode == SA_MODE_ECP ? 2LL * seg : mode == SA_MODE_SSPLIT ? (long long)seg : (long long)k_win + 1;
   if (range > Lmax) range = Lmax;
@@ -371,7 +371,7 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int Lmax, int d
       check_mode(mode, k_win, pi, M, seg) != SA_OK || mode == SA_MODE_WINDOW_BIDIR || mode == SA_MODE_ECP_FULL)
     return 0;
   int nw, chunk, mm;
-  decode_plan(Lmax, mode, k_win, pi, M, seg, &nw, &chunk, &mm);
+  decode_plan(Lmax, mode, k_win, pi, seg, &nw, &chunk, &mm);
   return round_up((size_t)B * Hq * (nw + 1) * (d + 4) * sizeof(float), 256);
 }
 
@@ -424,7 +424,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
   da.ws = (float *)workspace;
   da.B = B; da.Hq = Hq; da.Hkv = Hkv; da.Lmax = Lplan; da.d = d; da.dtype = dtype;
   da.mode = mode; da.k_win = k_win; da.pi = pi; da.M = M; da.seg = seg;
-  decode_plan(Lplan, mode, k_win, pi, M, seg, &da.n_wsplit, &da.chunk, &da.m_min);
+  decode_plan(Lplan, mode, k_win, pi, seg, &da.n_wsplit, &da.chunk, &da.m_min);
   da.nsplit = da.n_wsplit + 1;
   da.layout = layout; da.R = R; da.page_shift = page_shift; da.num_pages = num_pages; da.max_pages = max_pages;
   da.table = table;
