@@ -339,6 +339,41 @@ def bwd(q, k, v, alpha, o, lse, dO, *, mode, k_win: int = 0, pi: int = 0, M: int
     return dq, dk, dv, dalpha
 
 
+class _Attention(torch.autograd.Function):
+    """torch autograd over the library: the training forward (o and the row
+    log-sum-exp, sparse_attn_fwd_lse / _ex) and sparse_attn_bwd(_ex) for the
+    gradients.  No arithmetic here: both directions run in the HIP kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, alpha, out_gate, prm):
+        B, Hq, N, _ = q.shape
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        o = fwd(q, k, v, alpha, lse=lse, out_gate=out_gate, **prm)
+        ctx.prm = prm
+        ctx.save_for_backward(q, k, v, alpha, out_gate, o, lse)
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, alpha, out_gate, o, lse = ctx.saved_tensors
+        r = bwd(q, k, v, alpha, o, lse, dO.contiguous(), out_gate=out_gate, **ctx.prm)
+        dalpha = r[3] if ctx.needs_input_grad[3] else None
+        dgate = r[4] if out_gate is not None and ctx.needs_input_grad[4] else None
+        return r[0], r[1], r[2], dalpha, dgate, None
+
+
+def attention(q, k, v, alpha=None, *, mode, k_win: int = 0, pi: int = 0, M: int = 0, seg: int = 0,
+              score_scale: float = 0.0, out_gate=None):
+    """Differentiable prefill attention for training (torch autograd; bf16
+    q, k, v [B,H,N,d], contiguous, on the GPU): the forward keeps o and the
+    row log-sum-exp, the backward returns dq, dk, dv, dalpha (PI mode with
+    alpha) and d(out_gate).  Cosine scores or a gate network compose in the
+    caller: normalise q, k and pass the scale, or form alpha, and autograd
+    carries the gradients through them."""
+    prm = dict(mode=mode, k_win=int(k_win), pi=int(pi), M=int(M), seg=int(seg), score_scale=float(score_scale))
+    return _Attention.apply(q, k, v, alpha, out_gate, prm)
+
+
 def decode(q, k_cache, v_cache, cache_lens, alpha=None, *, mode, k_win: int = 0, pi: int = 0,
            M: int = 0, seg: int = 0, out=None, workspace=None, score_scale: float = 0.0,
            cosine: bool = False, gate_w=None, gate_b=None, out_gate=None, gate_w2=None, gate_b2=None):
