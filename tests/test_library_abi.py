@@ -134,6 +134,9 @@ def test_python_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         binding.fwd(q, q, q, mode="window", k_win=2)
+    qb = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError):   # the differentiable entry has no host path either
+        binding.attention(qb, qb, qb, mode="window", k_win=2)
 
 
 def fwd_lse(lib, lse=WS, **kw):
