@@ -1,7 +1,8 @@
 """The differentiable entry ``attention`` (torch autograd over the training
-forward and the backward) against the fp64 oracle, and the two compositions
-it is meant for: scaled cosine scores formed by normalising q and k in the
-caller, and a gate network on the query formed in the caller.  In both the
+forward and the backward) against the fp64 oracle, the looped block trained
+through its applications, and the two compositions it is meant for: scaled
+cosine scores formed by normalising q and k in the caller, and a gate network
+on the query formed in the caller.  In both the
 caller's own autograd carries the library's gradients (of the normalised
 rows, of alpha) back to its parameters; the references apply the same
 chain rule in fp64 to the oracle's gradients."""
@@ -143,3 +144,32 @@ def test_gate_network_by_composition():
     ref = torch.autograd.grad(a64, p64, grad_outputs=torch.from_numpy(np.asarray(ra, dtype=np.float64)))
     for name, got, r in zip(("w1", "b1", "w2", "b2"), params, ref):
         assert_grad_close(got.grad.cpu().numpy(), r.numpy(), "gate network d" + name)
+
+
+def test_looped_block_autograd():
+    # The looped block (LT2 section 2.2): V_{t+1} = O_t (bf16, as stored) with q
+    # and k fixed, trained through all T applications.  Reference: the oracle's
+    # forward chain (rounded to bf16 between applications, as the looped
+    # oracle does) and its backward applied in reverse, dq and dk summed over
+    # the applications and each application's dv fed to the one before.
+    w = Workload("ag_loop", "window", "bf16", 1, 2, 2, 600, 64, k_win=64, seed=189)
+    T = 3
+    q, k, v, _ = prefill_inputs(w)
+    dO = grad_output(w)
+    qd, kd, vd = leaf(q), leaf(k), leaf(v)
+    x = vd
+    for _ in range(T):
+        x = sa.attention(qd, kd, x, mode="window", k_win=w.k_win)
+    (x.float() * dO.to(DEV).float()).sum().backward()
+    torch.cuda.synchronize()
+    vs = [v]
+    for _ in range(T - 1):
+        vs.append(torch.from_numpy(oracle.fwd(q, k, vs[-1], mode="window", k_win=w.k_win)).float().bfloat16())
+    g = dO.float()
+    rq = rk = 0.0
+    for t in reversed(range(T)):
+        gq, gk, gv, _ = oracle.bwd(q, k, vs[t], None, g, mode="window", k_win=w.k_win)
+        rq, rk, g = rq + gq, rk + gk, torch.from_numpy(np.asarray(gv)).float()
+    assert_grad_close(qd.grad.float().cpu().numpy(), rq, "loop dq")
+    assert_grad_close(kd.grad.float().cpu().numpy(), rk, "loop dk")
+    assert_grad_close(vd.grad.float().cpu().numpy(), g.numpy(), "loop dv")
