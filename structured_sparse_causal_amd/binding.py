@@ -354,6 +354,7 @@ class _Attention(torch.autograd.Function):
         return o
 
     @staticmethod
+    @torch.autograd.function.once_differentiable
     def backward(ctx, dO):
         q, k, v, alpha, out_gate, o, lse = ctx.saved_tensors
         r = bwd(q, k, v, alpha, o, lse, dO.contiguous(), out_gate=out_gate, **ctx.prm)
