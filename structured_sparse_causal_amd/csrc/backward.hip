@@ -140,18 +140,36 @@ __device__ __forceinline__ bf16x4 lds_tr16(const bf16 *rows, int c0, int G, int 
   return as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)src));
 }
 
-// Four fp32 values x added to four bf16 values u (read from dst earlier) and
-// stored to dst: the sum rounded to bf16 once.
-__device__ __forceinline__ void add_old_bf16x4(bf16 *dst, ushort4 u, f32x4 x) {
-  u.x = f32_to_bf16_bits(bf16_to_f32(u.x) + x[0]);
-  u.y = f32_to_bf16_bits(bf16_to_f32(u.y) + x[1]);
-  u.z = f32_to_bf16_bits(bf16_to_f32(u.z) + x[2]);
-  u.w = f32_to_bf16_bits(bf16_to_f32(u.w) + x[3]);
-  *(ushort4 *)dst = u;
+// Gradient rows added back with 16-byte accesses: a 16 x D block in the 16x16
+// MFMA C layout (lane (G, t) holds values 16db + 4G + e of row t) is written
+// to the wave's LDS as fp32 rows of stride D + 4 floats, then each lane takes
+// the chunks 32kk + 8G .. +7 of row t (the layout of the operand loads), adds
+// the bf16 values read from the destination earlier in that layout, and
+// stores the sum rounded to bf16 once.  Callers order the LDS accesses
+// (wave_lds_sync) around stage_rows.
+template <int D>
+__device__ __forceinline__ void stage_rows(float *buf, const f32x4 (&x)[D / 16], float scale, int G, int t) {
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) *(f32x4 *)(buf + t * (D + 4) + 16 * db + 4 * G) = x[db] * scale;
 }
 
-// The same with the bf16 values read from dst now.
-__device__ __forceinline__ void add_bf16x4(bf16 *dst, f32x4 x) { add_old_bf16x4(dst, *(const ushort4 *)dst, x); }
+template <int D>
+__device__ __forceinline__ void add_rows(bf16 *dst_row, const float *buf, const bf16x8 (&old)[D / 32], int G, int t) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const f32x4 a = *(const f32x4 *)(buf + t * (D + 4) + 32 * kk + 8 * G);
+    const f32x4 b = *(const f32x4 *)(buf + t * (D + 4) + 32 * kk + 8 * G + 4);
+    const uint2 lo = pack_bf16x4((float)old[kk][0] + a[0], (float)old[kk][1] + a[1],
+                                 (float)old[kk][2] + a[2], (float)old[kk][3] + a[3]);
+    const uint2 hi = pack_bf16x4((float)old[kk][4] + b[0], (float)old[kk][5] + b[1],
+                                 (float)old[kk][6] + b[2], (float)old[kk][7] + b[3]);
+    *(uint4 *)(dst_row + 32 * kk + 8 * G) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// Bytes of a wave's fp32 staging rows.
+template <int D>
+constexpr int kStageBytes = 16 * (D + 4) * 4;
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -170,6 +188,7 @@ template <int D, bool WITH_Q>
 __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   constexpr int LD = D + 8, NK = D / 32, ND = D / 16;
   __shared__ __attribute__((aligned(16))) bf16 lds[4][(WITH_Q ? 3 : 2) * 16 * LD];
+  static_assert(2 * 16 * LD * 2 >= kStageBytes<D>, "the fp32 staging rows fit in the q and dO slabs");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int work = blockIdx.x * 4 + wave;
   if (work >= p.nwork_kv) return;  // no block-level barrier below: waves are independent
@@ -185,6 +204,8 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   // Rows past the chain re-read row r (in range: r < pi < N) and only meet
   // masked scores; loads are unconditional so they are issued together.
   const int ik = kvalid ? (int)ikl : r;
+  // a key with no query at period + m_min has no skip queries: its rows are left as the walks wrote them
+  const bool kpart = kvalid && ikl + (long long)p.m_min * p.pi < N;
   const bf16 *Kp = p.k + (size_t)bg * N * D, *Vp = p.v + (size_t)bg * N * D;
   bf16 *qs = lds[wave], *os = qs + 16 * LD, *ks = os + 16 * LD;
 
@@ -196,11 +217,13 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
   }
   // the dk, dv rows the walks wrote, read now so the add at the end waits on nothing
   const size_t krow = (size_t)bg * N + ik;
-  ushort4 dk0[ND], dv0[ND];
+  bf16x8 dk0[NK], dv0[NK];
+  if (kpart) {
 #pragma unroll
-  for (int db = 0; db < ND; ++db) {
-    dk0[db] = *(const ushort4 *)(p.dk + krow * D + 16 * db + 4 * G);
-    dv0[db] = *(const ushort4 *)(p.dv + krow * D + 16 * db + 4 * G);
+    for (int kk = 0; kk < NK; ++kk) {
+      dk0[kk] = *(const bf16x8 *)(p.dk + krow * D + 32 * kk + 8 * G);
+      dv0[kk] = *(const bf16x8 *)(p.dv + krow * D + 32 * kk + 8 * G);
+    }
   }
   if (WITH_Q) {
 #pragma unroll
@@ -222,11 +245,12 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
       const bool qvalid = iql < N;
       const int iq = qvalid ? (int)iql : r;   // in-range row; masked below
       const size_t qrow = bh * N + iq;
-      bf16x8 qa[NK], oa[NK];
+      bf16x8 qa[NK], oa[NK], dqo[NK];
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         qa[kk] = *(const bf16x8 *)(Qp + (size_t)iq * D + 32 * kk + 8 * G);
         oa[kk] = *(const bf16x8 *)(Op + (size_t)iq * D + 32 * kk + 8 * G);
+        if (WITH_Q) dqo[kk] = *(const bf16x8 *)(p.dq + qrow * D + 32 * kk + 8 * G);
       }
       const float c0 = -p.lse[qrow] * kLog2e;
       const float Dq = p.Dv[qrow];
@@ -287,21 +311,27 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
 #pragma unroll
         for (int db = 0; db < ND; ++db)
           aq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr16<LD>(ks, 16 * db, G, t), dsb, f32x4{}, 0, 0, 0);
+        // the q and dO slabs are free once the dV and dK products have read them
+        float *buf = (float *)qs;
+        wave_lds_sync();
+        stage_rows<D>(buf, aq, p.scale, G, t);
+        wave_lds_sync();
         if (qvalid) {
-          bf16 *dst = p.dq + qrow * D;
-#pragma unroll
-          for (int db = 0; db < ND; ++db) add_bf16x4(dst + 16 * db + 4 * G, aq[db] * p.scale);
+          add_rows<D>(p.dq + qrow * D, buf, dqo, G, t);
           if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
         }
       }
     }
   }
-  if (!kvalid) return;
-#pragma unroll
-  for (int db = 0; db < ND; ++db) {
-    add_old_bf16x4(p.dk + krow * D + 16 * db + 4 * G, dk0[db], adk[db] * p.scale);
-    add_old_bf16x4(p.dv + krow * D + 16 * db + 4 * G, dv0[db], adv[db]);
-  }
+  float *buf = (float *)qs;
+  wave_lds_sync();  // the last tile's transposed reads are done
+  stage_rows<D>(buf, adk, p.scale, G, t);
+  wave_lds_sync();
+  if (kpart) add_rows<D>(p.dk + krow * D, buf, dk0, G, t);
+  wave_lds_sync();
+  stage_rows<D>(buf, adv, 1.0f, G, t);
+  wave_lds_sync();
+  if (kpart) add_rows<D>(p.dv + krow * D, buf, dv0, G, t);
 }
 
 // Query-stationary (residue chains longer than one tile): one wave per
@@ -310,7 +340,9 @@ __global__ __launch_bounds__(256) void skip_bwd_kv_kernel(Params p) {
 template <int D>
 __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   constexpr int LD = D + 8, NK = D / 32, ND = D / 16;
-  __shared__ __attribute__((aligned(16))) bf16 lds[4][16 * LD];
+  // per wave: the K rows for the transposed reads, then the fp32 staging rows
+  __shared__ __attribute__((aligned(16))) float lds[4][16 * (D + 4)];
+  static_assert(16 * LD * 2 <= kStageBytes<D>, "the K slab fits in the staging rows");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int work = blockIdx.x * 4 + wave;
   if (work >= p.nwork_q) return;  // no block-level barrier below
@@ -326,12 +358,13 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   const int iq = qvalid ? (int)iql : r;   // in-range row (r < pi < N); masked below
   const size_t qrow = bh * N + iq;
   const bf16 *Kp = p.k + (size_t)(b * p.Hkv + g) * N * D, *Vp = p.v + (size_t)(b * p.Hkv + g) * N * D;
-  bf16 *ks = lds[wave];
-  bf16x8 qa[NK], oa[NK];
+  bf16 *ks = (bf16 *)lds[wave];
+  bf16x8 qa[NK], oa[NK], dqo[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     qa[kk] = *(const bf16x8 *)(p.q + qrow * D + 32 * kk + 8 * G);
     oa[kk] = *(const bf16x8 *)(p.dO + qrow * D + 32 * kk + 8 * G);
+    dqo[kk] = *(const bf16x8 *)(p.dq + qrow * D + 32 * kk + 8 * G);
   }
   const float c0 = -p.lse[qrow] * kLog2e;
   const float Dq = p.Dv[qrow];
@@ -377,9 +410,12 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
   }
   da += wave_shfl_xor(da, 16);
   da += wave_shfl_xor(da, 32);
+  float *buf = lds[wave];
+  wave_lds_sync();  // the last tile's transposed reads are done
+  stage_rows<D>(buf, aq, p.scale, G, t);
+  wave_lds_sync();
   if (!qvalid) return;
-#pragma unroll
-  for (int db = 0; db < ND; ++db) add_bf16x4(p.dq + qrow * D + 16 * db + 4 * G, aq[db] * p.scale);
+  add_rows<D>(p.dq + qrow * D, buf, dqo, G, t);
   if (G == 0 && p.dalpha != nullptr) p.dalpha[qrow] = da / al;
 }
 
