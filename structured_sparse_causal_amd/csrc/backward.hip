@@ -420,23 +420,23 @@ __global__ __launch_bounds__(256) void skip_bwd_q_kernel(Params p) {
 }
 
 // Store 16 accumulator values of a 32x32 C tile (rows 8(j/4) + 4h + j%4 of the
-// 32-row block db, column = this lane) as bf16, scaled.
+// 32-row block db, column = this lane) as bf16, scaled, with 16-byte stores
+// (half h writes elements 16jp + 8h .. +7 of each 32-block).  Both halves of
+// a lane pair must be active.
 template <int D>
 __device__ __forceinline__ void store_rows_bf16(bf16 *dst, const f32x16 (&acc)[D / 32], float scale, int h) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const int dim = 32 * db + 8 * j4 + 4 * h;
-      float x[4];
+    for (int jp = 0; jp < 2; ++jp) {
+      uint2 pk[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * scale;
-      ushort4 u;
-      u.x = f32_to_bf16_bits(x[0]);
-      u.y = f32_to_bf16_bits(x[1]);
-      u.z = f32_to_bf16_bits(x[2]);
-      u.w = f32_to_bf16_bits(x[3]);
-      *(ushort4 *)(dst + dim) = u;
+      for (int j = 0; j < 2; ++j) {
+        const int j4 = 2 * jp + j;
+        pk[j] = pack_bf16x4(acc[db][4 * j4] * scale, acc[db][4 * j4 + 1] * scale,
+                            acc[db][4 * j4 + 2] * scale, acc[db][4 * j4 + 3] * scale);
+      }
+      *(uint4 *)(dst + 32 * db + 16 * jp + 8 * h) = half_regroup(pk[0], pk[1]);
     }
 }
 

@@ -129,6 +129,37 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 16-byte row chunks from the 32x32 MFMA C layout.  There the wave half h
+// (lane >> 5) holds elements 4h..4h+3 of every 8-element group of a row.  For
+// two groups lo, hi (four bf16 each, as uint2), half_regroup returns in half 0
+// the whole group lo and in half 1 the whole group hi (one v_permlane32_swap
+// per dword: half 0's hi part and half 1's lo part change places).  It is its
+// own inverse: half_ungroup takes a 16-byte chunk loaded that way back to the
+// C layout.  Both halves of a lane pair must be active.
+__device__ __forceinline__ uint4 half_regroup(uint2 lo, uint2 hi) {
+  const auto a = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+  return make_uint4(a[0], b[0], a[1], b[1]);
+}
+
+__device__ __forceinline__ void half_ungroup(uint4 u, uint2 &lo, uint2 &hi) {
+  const auto a = __builtin_amdgcn_permlane32_swap(u.x, u.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(u.y, u.w, false, false);
+  lo = make_uint2(a[0], b[0]);
+  hi = make_uint2(a[1], b[1]);
+}
+
+// The same for the 16x16 C layout, where lane row G (lane >> 4) holds elements
+// 4G..4G+3 of each 16-element block: for blocks x (even) and y (odd) of one
+// 32-element span, rows 0 and 1 exchange (x of row 1, y of row 0) and so do
+// rows 2 and 3 (one v_permlane16_swap per dword).  Row G then holds the 8
+// consecutive elements starting at 8 (G >> 1) + 16 (G & 1) of the span.
+__device__ __forceinline__ uint4 row_regroup(uint2 x, uint2 y) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+  return make_uint4(a[0], b[0], a[1], b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Row-major bf16 tiles (64 rows) go from HBM straight into LDS
 // (global_load_lds_dwordx4: no staging registers), rows unpadded with the

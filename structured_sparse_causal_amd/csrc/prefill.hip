@@ -424,12 +424,18 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const ushort4 u = *(const ushort4 *)(ap + 32 * db + 8 * j4 + 4 * h);
-        acc[db][4 * j4 + 0] = bf16_to_f32(u.x);
-        acc[db][4 * j4 + 1] = bf16_to_f32(u.y);
-        acc[db][4 * j4 + 2] = bf16_to_f32(u.z);
-        acc[db][4 * j4 + 3] = bf16_to_f32(u.w);
+      for (int jp = 0; jp < 2; ++jp) {
+        // 16-byte loads, back to the accumulator layout (half h: 4h..4h+3 of each 8)
+        uint2 pk[2];
+        half_ungroup(*(const uint4 *)(ap + 32 * db + 16 * jp + 8 * h), pk[0], pk[1]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int j4 = 2 * jp + j;
+          acc[db][4 * j4 + 0] = __uint_as_float(pk[j].x << 16);
+          acc[db][4 * j4 + 1] = __uint_as_float(pk[j].x & 0xffff0000u);
+          acc[db][4 * j4 + 2] = __uint_as_float(pk[j].y << 16);
+          acc[db][4 * j4 + 3] = __uint_as_float(pk[j].y & 0xffff0000u);
+        }
       }
   }
 
@@ -642,21 +648,32 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
   const float inv = 1.0f / l_tot;
   bf16 *op = (bf16 *)p.o + ((size_t)bh * N + qi) * D;
   const bf16 *gp = p.opt.out_gate != nullptr ? (const bf16 *)p.opt.out_gate + ((size_t)bh * N + qi) * D : nullptr;
+  // The wave half once more, from the lane count: a copy of h kept from
+  // before the tile walk held a register through it (at d = 64 the register
+  // that keeps four waves per SIMD).
+  const int hs = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      float x[4];
+    for (int jp = 0; jp < 2; ++jp) {
+      uint2 pk[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
-      if (gp != nullptr) {   // output gate o * sigmoid(g)
-        const ushort4 gu = *(const ushort4 *)(gp + 32 * db + 8 * j4 + 4 * h);
-        x[0] *= sigmoidf_fast(bf16_to_f32(gu.x));
-        x[1] *= sigmoidf_fast(bf16_to_f32(gu.y));
-        x[2] *= sigmoidf_fast(bf16_to_f32(gu.z));
-        x[3] *= sigmoidf_fast(bf16_to_f32(gu.w));
+      for (int j = 0; j < 2; ++j) {
+        const int j4 = 2 * jp + j;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
+        if (gp != nullptr) {   // output gate o * sigmoid(g)
+          const ushort4 gu = *(const ushort4 *)(gp + 32 * db + 8 * j4 + 4 * h);
+          x[0] *= sigmoidf_fast(bf16_to_f32(gu.x));
+          x[1] *= sigmoidf_fast(bf16_to_f32(gu.y));
+          x[2] *= sigmoidf_fast(bf16_to_f32(gu.z));
+          x[3] *= sigmoidf_fast(bf16_to_f32(gu.w));
+        }
+        pk[j] = pack_bf16x4(x[0], x[1], x[2], x[3]);
       }
-      *(uint2 *)(op + 32 * db + 8 * j4 + 4 * h) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+      // 16-byte stores: half hs writes elements 16 jp + 8 hs .. +7 of the 32-block
+      *(uint4 *)(op + 32 * db + 16 * jp + 8 * hs) = half_regroup(pk[0], pk[1]);
     }
 }
 

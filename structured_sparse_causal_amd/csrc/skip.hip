@@ -210,9 +210,12 @@ __global__ __launch_bounds__(64 * kSkipWaves) void skip_bf16_kernel(Params p) {
   // Accumulators are stored in bf16 (the I/O precision): half the workspace
   // traffic; the relative rounding (2^-9) applies to the skip share only.
   bf16 *ap = (bf16 *)p.acc + row * D;
+  // 16-byte stores: the two 16-blocks of each 32-span regrouped between lane rows
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    *(uint2 *)(ap + 16 * db + 4 * G) = pack_bf16x4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  for (int dp = 0; dp < D / 32; ++dp)
+    *(uint4 *)(ap + 32 * dp + 8 * (G >> 1) + 16 * (G & 1)) =
+        row_regroup(pack_bf16x4(acc[2 * dp][0], acc[2 * dp][1], acc[2 * dp][2], acc[2 * dp][3]),
+                    pack_bf16x4(acc[2 * dp + 1][0], acc[2 * dp + 1][1], acc[2 * dp + 1][2], acc[2 * dp + 1][3]));
 }
 
 // fp32 I/O: one thread per query row, plain loops.
