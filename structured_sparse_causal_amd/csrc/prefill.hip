@@ -652,10 +652,20 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
   // before the tile walk held a register through it (at d = 64 the register
   // that keeps four waves per SIMD).
   const int hs = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
+  // Output gate rows, all loaded (16 bytes per lane) before any is used.
+  uint4 gq[NDB][2];
+  if (gp != nullptr) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) gq[db][jp] = *(const uint4 *)(gp + 32 * db + 16 * jp + 8 * hs);
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
+      uint2 gk[2];
+      if (gp != nullptr) half_ungroup(gq[db][jp], gk[0], gk[1]);   // back to the accumulator layout
       uint2 pk[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -664,11 +674,10 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * j4 + e] * inv;
         if (gp != nullptr) {   // output gate o * sigmoid(g)
-          const ushort4 gu = *(const ushort4 *)(gp + 32 * db + 8 * j4 + 4 * h);
-          x[0] *= sigmoidf_fast(bf16_to_f32(gu.x));
-          x[1] *= sigmoidf_fast(bf16_to_f32(gu.y));
-          x[2] *= sigmoidf_fast(bf16_to_f32(gu.z));
-          x[3] *= sigmoidf_fast(bf16_to_f32(gu.w));
+          x[0] *= sigmoidf_fast(__uint_as_float(gk[j].x << 16));
+          x[1] *= sigmoidf_fast(__uint_as_float(gk[j].x & 0xffff0000u));
+          x[2] *= sigmoidf_fast(__uint_as_float(gk[j].y << 16));
+          x[3] *= sigmoidf_fast(__uint_as_float(gk[j].y & 0xffff0000u));
         }
         pk[j] = pack_bf16x4(x[0], x[1], x[2], x[3]);
       }
