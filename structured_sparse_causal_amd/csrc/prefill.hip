@@ -418,8 +418,9 @@ __global__ __launch_bounds__(256, (D == 128 && TBN == 32) ? 3 : 2) void prefill_
   // Seed with the skip-key partial state (pi-Attention union, one softmax).
   if (p.skip_ml != nullptr && qvalid && qi >= p.skip_first) {
     const size_t row = (size_t)bh * N + qi;
-    m_run = p.skip_ml[2 * row];
-    if (h == 0) l_run = p.skip_ml[2 * row + 1];
+    const float2 ml = *(const float2 *)(p.skip_ml + 2 * row);
+    m_run = ml.x;
+    if (h == 0) l_run = ml.y;
     const bf16 *ap = (const bf16 *)p.skip_acc + row * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -203,10 +203,7 @@ __global__ __launch_bounds__(64 * kSkipWaves) void skip_bf16_kernel(Params p) {
   l_run += wave_shfl_xor(l_run, 32);
   if (!qvalid) return;
   const size_t row = (size_t)bh * N + iq;
-  if (G == 0) {
-    p.ml[2 * row] = m_run;
-    p.ml[2 * row + 1] = l_run;
-  }
+  if (G == 0) *(float2 *)(p.ml + 2 * row) = make_float2(m_run, l_run);
   // Accumulators are stored in bf16 (the I/O precision): half the workspace
   // traffic; the relative rounding (2^-9) applies to the skip share only.
   bf16 *ap = (bf16 *)p.acc + row * D;
