@@ -8,8 +8,14 @@ above the window.  Every output element is compared with the fp64 oracle.
 Forty-eight more (bf16) run the training forward and the backward and compare
 every gradient element with the oracle's fp64 chain rule, and forty-eight
 decode cases with ragged cache lengths compare every output element.
+
+SA_RANDOM_SHAPES="seed,n_fwd,n_bwd,n_dec" draws other (or more) cases from the
+same generators: the seed is added to each generator's own, the counts replace
+96, 48 and 48.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -23,9 +29,11 @@ from structured_sparse_causal_amd.inputs import Workload, prefill_inputs
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 MODES = ["pi", "window", "ecp", "window_bidir", "ssplit", "ecp_full"]
+_draw = [int(x) for x in os.environ.get("SA_RANDOM_SHAPES", "0,96,48,48").split(",")]
+SEED_SHIFT, N_FWD, N_BWD, N_DEC = _draw
 
 
-def _cases(n=96, seed=2024):
+def _cases(n=N_FWD, seed=2024 + SEED_SHIFT):
     rng = np.random.default_rng(seed)
     out = []
     for idx in range(n):
@@ -42,7 +50,7 @@ def _cases(n=96, seed=2024):
         M = int(rng.integers(0, 12)) if mode == "pi" else 0
         out.append(Workload("rand%02d_%s_%s_d%d" % (idx, mode, dtype, d), mode, dtype, B, hq, hkv, N, d,
                             k_win=k_win, pi=pi, M=M, seg=seg, scale_inputs=bool(rng.random() < 0.5),
-                            seed=500 + idx))
+                            seed=500 + idx + SEED_SHIFT))
     return out
 
 
@@ -57,7 +65,7 @@ def test_random_shape(w):
     assert_close(o.float().cpu().numpy(), ref, w.dtype, w.name)
 
 
-def _bwd_cases(n=48, seed=4048):
+def _bwd_cases(n=N_BWD, seed=4048 + SEED_SHIFT):
     rng = np.random.default_rng(seed)
     out = []
     for idx in range(n):
@@ -69,7 +77,7 @@ def _bwd_cases(n=48, seed=4048):
         out.append(Workload("rbwd%02d_%s_d%d" % (idx, mode, d), mode, "bf16", 1, hq, hkv, N, d,
                             k_win=int(rng.integers(0, N + 50)), pi=int(rng.integers(1, max(2, N // 3 + 2))),
                             M=int(rng.integers(0, 10)) if mode == "pi" else 0,
-                            seg=int(rng.integers(1, max(2, N // 2 + 64))), seed=700 + idx))
+                            seg=int(rng.integers(1, max(2, N // 2 + 64))), seed=700 + idx + SEED_SHIFT))
     return out
 
 
@@ -98,7 +106,7 @@ def test_random_shape_backward(w):
         assert_grad_close(da.cpu().numpy(), ra, w.name + " dalpha")
 
 
-def _decode_cases(n=48, seed=8096):
+def _decode_cases(n=N_DEC, seed=8096 + SEED_SHIFT):
     rng = np.random.default_rng(seed)
     out = []
     for idx in range(n):
@@ -110,7 +118,7 @@ def _decode_cases(n=48, seed=8096):
         out.append(Workload("rdec%02d_%s_d%d" % (idx, mode, d), mode, "bf16", int(rng.integers(1, 40)), hq, hkv, L,
                             d, k_win=int(rng.integers(0, L + 50)), pi=int(rng.integers(1, max(2, L // 3 + 2))),
                             M=int(rng.integers(0, 16)) if mode == "pi" else 0,
-                            seg=int(rng.integers(1, max(2, L // 2 + 64))), decode=True, seed=900 + idx))
+                            seg=int(rng.integers(1, max(2, L // 2 + 64))), decode=True, seed=900 + idx + SEED_SHIFT))
     return out
 
 
